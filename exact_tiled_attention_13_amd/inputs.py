@@ -1,0 +1,81 @@
+"""Seeded synthetic inputs and the named attention workloads.
+
+This module holds no attention arithmetic. It is the only code that both the
+HIP path's callers (tests, bench) and the CPU oracle's callers share: it draws
+the tensors, and each side then computes on identical values.
+
+Recipe: a CPU ``torch.Generator`` seeded per workload draws Q, then K, then V,
+then dO, each ``randn(B, N, H, d)`` in float32 (iid N(0, 1), no structure),
+then rounds to bfloat16 with round-to-nearest-even unless the workload is
+fp32. Layout is ``[B, N, H, d]``, d fastest, contiguous.
+
+The workload sweep follows the kernel benchmark that the page
+"FlashAttention-2: atención eficiente en GPU para contextos largos" describes
+in section "Qué significa la mejora de aproximadamente dos veces": sequence
+lengths from 512 to about 16k, head dimensions 64 and 128, with and without
+the causal mask, at 16k tokens per batch. It names no dataset; these seeded
+tensors stand in for its inputs.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "fp32" or "bf16"
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: tuple       # masks the workload is run with
+    backward: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(d), rounded to fp32 (the value the library receives)."""
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.N
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("fwd_fp32_b1_h2_n128_d64", "fp32", 1, 2, 128, 64, (False,), False, 1001),
+        Workload("fwd_bf16_b32_h32_n512_d64", "bf16", 32, 32, 512, 64, (False, True), False, 1002),
+        Workload("fwd_bf16_b8_h16_n2048_d128", "bf16", 8, 16, 2048, 128, (True,), False, 1003),
+        Workload("fwd_bf16_b1_h16_n16384_d128", "bf16", 1, 16, 16384, 128, (False, True), False, 1004),
+        Workload("bwd_bf16_b4_h16_n4096_d128", "bf16", 4, 16, 4096, 128, (True,), True, 1005),
+    ]
+}
+
+# Backward timed at the long-context shape (batch 1, 16 heads, 16k tokens, d 128).
+BWD_LONG = Workload("bwd_bf16_b1_h16_n16384_d128", "bf16", 1, 16, 16384, 128, (False, True), True, 1004)
+
+
+def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0, with_do: bool = False):
+    """Draw Q, K, V (and dO) on the CPU. Returns a tuple of CPU tensors [B, N, H, d].
+
+    dtype "bf16" rounds the float32 draws to bfloat16 (RNE); "fp32" keeps them.
+    """
+    g = torch.Generator().manual_seed(seed)
+    n = 4 if with_do else 3
+    out = []
+    for _ in range(n):
+        t = torch.randn(B, N, H, d, dtype=torch.float32, generator=g)
+        out.append(t.to(torch.bfloat16) if dtype == "bf16" else t)
+    return tuple(out)
+
+
+def make_workload(w: Workload):
+    """Inputs of a named workload: (q, k, v) or (q, k, v, do) on the CPU."""
+    return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, with_do=w.backward)
