@@ -1,0 +1,218 @@
+"""Benchmark of exact tiled attention (forward + backward) on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input
+at the long-context shape (batch 1, 16 heads, 16384 tokens, head dim 128,
+bf16): forward and backward without the causal mask, then forward and
+backward with it. Counted FLOP per pass: forward 4*B*H*N^2*d, backward 2.5x
+that, both halved under the causal mask; the value is the step's counted
+FLOP divided by its wall time, in TFLOP/s.
+
+Each kernel launch is bracketed by HIP events on the stream it runs on, so
+the average duration of every kernel is measured inside the timed region;
+the dominant one is reported against its roofline. The fp64 CPU oracle is
+timed on a bounded sample of the same workload as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s and % bf16 MFMA peak, 16k tokens/batch, d=64/128"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+
+
+def counted_fwd(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def cpu_baseline(q, k, v, do, scale):
+    """Time the fp64 oracle on a bounded sample of the workload (rank 0 only)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attn_bwd_head, attn_fwd_rows
+
+    B, N, H, d = q.shape
+    rows = np.arange(0, N, N // 2048)[:2048]
+    qh, kh, vh = (x[0, :, 0].double().numpy() for x in (q, k, v))
+    nb = 4096
+    qb, kb, vb, gb = (x[0, :nb, 1].double().numpy() for x in (q, k, v, do))
+    t0 = time.perf_counter()
+    attn_fwd_rows(qh, kh, vh, rows, False, scale)
+    t1 = time.perf_counter()
+    attn_bwd_head(qb, kb, vb, gb, False, scale)
+    t2 = time.perf_counter()
+    flops = 4.0 * len(rows) * N * d + 2.5 * counted_fwd(1, 1, nb, d, False)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {
+        "value": flops / (t2 - t0) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: forward of {len(rows)} query rows x {N} keys of one head "
+                   f"(non-causal, {t1 - t0:.2f} s) plus the full backward of one head truncated to its first "
+                   f"{nb} tokens ({t2 - t1:.2f} s); same inputs and counted-FLOP formula as the GPU step"),
+        "seconds": t2 - t0,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels shard by heads with no communication, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_13_amd as fa
+    from exact_tiled_attention_13_amd.inputs import BWD_LONG, make_workload
+
+    w = BWD_LONG
+    B, H, N, d = w.B, w.H, w.N, w.d
+    dev = torch.device("cuda:0")
+    q, k, v, do = make_workload(w)
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    masks = (False, True)
+    bufs = {}
+    for c in masks:
+        bufs[c] = dict(o=torch.empty_like(qd), lse=torch.empty((B, H, N), dtype=torch.float32, device=dev),
+                       dd=torch.empty((B, H, N), dtype=torch.float32, device=dev), dq=torch.empty_like(qd),
+                       dk=torch.empty_like(kd), dv=torch.empty_like(vd))
+    scale = w.scale
+    stream = torch.cuda.current_stream(dev)
+
+    names = []
+    for c in masks:
+        tag = "causal" if c else "noncausal"
+        names += [f"fwd_{tag}", f"bwd_prep_{tag}", f"bwd_dkdv_{tag}", f"bwd_dq_{tag}"]
+
+    def launches(c):
+        b = bufs[c]
+        return [
+            lambda: fa.attn_fwd(qd, kd, vd, c, scale, o=b["o"], lse=b["lse"]),
+            lambda: fa.attn_bwd_prep(b["o"], dod, dd=b["dd"]),
+            lambda: fa.attn_bwd_dkdv(qd, kd, vd, dod, b["lse"], b["dd"], c, scale, dk=b["dk"], dv=b["dv"]),
+            lambda: fa.attn_bwd_dq(qd, kd, vd, dod, b["lse"], b["dd"], c, scale, dq=b["dq"]),
+        ]
+
+    calls = [f for c in masks for f in launches(c)]
+
+    def step(events=None):
+        for i, f in enumerate(calls):
+            if events is not None:
+                events[i][0].record(stream)
+            f()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    kern_ms = {n: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+               for i, n in enumerate(names)}
+
+    # Algorithmic work per launch.
+    work = {}
+    for c in masks:
+        tag = "causal" if c else "noncausal"
+        f1 = counted_fwd(B, H, N, d, c) / 2           # one N x N x d product
+        work[f"fwd_{tag}"] = ("mfma", 2 * f1)
+        work[f"bwd_dkdv_{tag}"] = ("mfma", 4 * f1)     # S (recompute), dP, dV, dK
+        work[f"bwd_dq_{tag}"] = ("mfma", 1 * f1)       # dQ (S, dP recomputed again: not counted)
+        work[f"bwd_prep_{tag}"] = ("hbm", 2.0 * B * N * H * d * 2 + 4.0 * B * H * N)
+    step_flops = sum(counted_fwd(B, H, N, d, c) * 3.5 for c in masks)
+
+    breakdown = {}
+    for n in names:
+        kind, amount = work[n]
+        rate = amount / (kern_ms[n] * 1e-3)
+        if kind == "mfma":
+            breakdown[n] = {"ms": round(kern_ms[n], 4), "tflops": round(rate / 1e12, 1),
+                            "frac_bf16_peak": round(rate / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        else:
+            breakdown[n] = {"ms": round(kern_ms[n], 4), "gbs": round(rate / 1e9, 1),
+                            "frac_hbm_peak": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
+    passes = {}
+    for c in masks:
+        tag = "causal" if c else "noncausal"
+        fms = kern_ms[f"fwd_{tag}"]
+        bms = kern_ms[f"bwd_prep_{tag}"] + kern_ms[f"bwd_dkdv_{tag}"] + kern_ms[f"bwd_dq_{tag}"]
+        ff = counted_fwd(B, H, N, d, c)
+        passes[f"fwd_{tag}"] = {"ms": round(fms, 4), "tflops": round(ff / fms / 1e9, 1),
+                                "frac_bf16_peak": round(ff / fms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        passes[f"bwd_{tag}"] = {"ms": round(bms, 4), "tflops": round(2.5 * ff / bms / 1e9, 1),
+                                "frac_bf16_peak": round(2.5 * ff / bms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+    dom = max(names, key=lambda n: kern_ms[n])
+    kind, amount = work[dom]
+    achieved = amount / (kern_ms[dom] * 1e-3)
+    if kind == "mfma":
+        roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = dom
+    roof["work_per_launch"] = amount
+    roof["avg_launch_ms"] = round(kern_ms[dom], 4)
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention forward+backward, non-causal then causal, B=1 H=16 N=16384 d=128 "
+                               "(16k tokens per batch), bf16 in / fp32 accumulate",
+                   "B": B, "H": H, "N": N, "d": d, "causal": list(masks), "seed": w.seed},
+        "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "passes": passes,
+        "kernels": breakdown,
+        "roofline": roof,
+        "gpu": torch.cuda.get_device_name(dev),
+        "max_memory_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

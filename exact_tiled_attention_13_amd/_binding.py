@@ -1,0 +1,213 @@
+"""ctypes binding of libfa_mi355x.so (C ABI in include/fa_mi355x.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the attention computation runs in the library's HIP
+kernels. There is no fallback: if the library is missing or a call is
+rejected, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_WORKSPACE = 3
+FA_ERR_HIP = 4
+
+EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_prep",
+            "attn_bwd_dkdv", "attn_bwd_dq", "fa_status_string")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A libfa_mi355x entry point returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m exact_tiled_attention_13_amd.build` "
+                    "(or __graft_entry__.build()); there is no fallback path")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+            L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+            L.attn_fwd.restype = ci
+            L.attn_fwd_fp32.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+            L.attn_fwd_fp32.restype = ci
+            L.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci]
+            L.attn_bwd_workspace_size.restype = sz
+            L.attn_bwd.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, cf, vp]
+            L.attn_bwd.restype = ci
+            L.attn_bwd_prep.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp]
+            L.attn_bwd_prep.restype = ci
+            L.attn_bwd_dkdv.argtypes = [vp] * 8 + [ci, ci, ci, ci, ci, cf, vp]
+            L.attn_bwd_dkdv.restype = ci
+            L.attn_bwd_dq.argtypes = [vp] * 7 + [ci, ci, ci, ci, ci, cf, vp]
+            L.attn_bwd_dq.restype = ci
+            L.fa_status_string.argtypes = [ci]
+            L.fa_status_string.restype = ctypes.c_char_p
+            _lib = L
+        return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != FA_OK:
+        raise FaError(fn, status)
+
+
+def _shape(q: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError(f"expected [B, N, H, d] tensors, got shape {tuple(q.shape)}")
+    B, N, H, d = q.shape
+    return B, N, H, d
+
+
+def _expect(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device} (contiguous={t.is_contiguous()})")
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None):
+    """bf16 forward. q, k, v: contiguous bf16 [B, N, H, d] on one GPU. Returns (o, lse)."""
+    B, N, H, d = _shape(q)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _expect("o", o, (B, N, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    s = default_scale(d) if scale is None else float(scale)
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), s,
+                        _stream(dev))
+    _check("attn_fwd", st)
+    return o, lse
+
+
+def attn_fwd_fp32(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None):
+    """fp32 forward. q, k, v: contiguous fp32 [B, N, H, d]. Returns (o, lse)."""
+    B, N, H, d = _shape(q)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _expect(name, t, (B, N, H, d), torch.float32, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _expect("o", o, (B, N, H, d), torch.float32, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    s = default_scale(d) if scale is None else float(scale)
+    st = lib().attn_fwd_fp32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), s,
+                             _stream(dev))
+    _check("attn_fwd_fp32", st)
+    return o, lse
+
+
+def attn_bwd_workspace_size(B: int, H: int, N: int, d: int, causal: bool = False) -> int:
+    return int(lib().attn_bwd_workspace_size(B, H, N, d, int(bool(causal))))
+
+
+def attn_bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """bf16 backward. Returns (dq, dk, dv), each contiguous bf16 [B, N, H, d]."""
+    B, N, H, d = _shape(q)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    need = attn_bwd_workspace_size(B, H, N, d, causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    s = default_scale(d) if scale is None else float(scale)
+    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d,
+                        int(bool(causal)), s, _stream(dev))
+    _check("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_bwd_prep(o, do, dd=None):
+    """dd[b, h, i] = dO_i . O_i (fp32 [B, H, N]). Returns dd."""
+    B, N, H, d = _shape(o)
+    dev = o.device
+    _expect("o", o, (B, N, H, d), torch.bfloat16, dev)
+    _expect("do", do, (B, N, H, d), torch.bfloat16, dev)
+    dd = torch.empty((B, H, N), dtype=torch.float32, device=dev) if dd is None else dd
+    _expect("dd", dd, (B, H, N), torch.float32, dev)
+    _check("attn_bwd_prep", lib().attn_bwd_prep(_ptr(o), _ptr(do), _ptr(dd), B, H, N, d, _stream(dev)))
+    return dd
+
+
+def attn_bwd_dkdv(q, k, v, do, lse, dd, causal: bool = False, scale: float | None = None, dk=None, dv=None):
+    """dK and dV from the forward inputs, dO, the forward's LSE and dd. Returns (dk, dv)."""
+    B, N, H, d = _shape(q)
+    dev = q.device
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dk", dk), ("dv", dv)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    _expect("dd", dd, (B, H, N), torch.float32, dev)
+    s = default_scale(d) if scale is None else float(scale)
+    _check("attn_bwd_dkdv", lib().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dd),
+                                                _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), s,
+                                                _stream(dev)))
+    return dk, dv
+
+
+def attn_bwd_dq(q, k, v, do, lse, dd, causal: bool = False, scale: float | None = None, dq=None):
+    """dQ from the forward inputs, dO, the forward's LSE and dd. Returns dq."""
+    B, N, H, d = _shape(q)
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dq", dq)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    _expect("dd", dd, (B, H, N), torch.float32, dev)
+    s = default_scale(d) if scale is None else float(scale)
+    _check("attn_bwd_dq", lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dd), _ptr(dq),
+                                            B, H, N, d, int(bool(causal)), s, _stream(dev)))
+    return dq

@@ -1,0 +1,162 @@
+// api.cpp -- the C ABI of libfa_mi355x (declared in include/fa_mi355x.h).
+//
+// Validates every argument before touching HIP, derives the kernel
+// constants (base-2 softmax scale, sign folding) and calls the launchers.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa_mi355x.h"
+#include "kernels.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int B, int H, int N, int d, float scale) {
+    if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const long long per_batch = (long long)N * H * d;
+    if (per_batch >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    if ((long long)B * per_batch >= (1LL << 40)) return FA_ERR_INVALID_ARG;
+    // Grid sizes: (ceil(N/128) * B * H) workgroups must fit a 32-bit grid.
+    if ((long long)((N + 127) / 128) * B * H >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+void fill_scale(float scale, float& c2, uint32_t& qsign, float& qsign_f) {
+    c2 = fabsf(scale) * fa::kLog2e;
+    const bool neg = signbit(scale) && scale != 0.0f;
+    qsign = neg ? 0x80008000u : 0u;
+    qsign_f = neg ? -1.0f : 1.0f;
+}
+
+size_t dd_bytes(int B, int H, int N) {
+    const size_t raw = (size_t)B * H * N * sizeof(float);
+    return (raw + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+             int causal, float scale, hipStream_t stream) {
+    int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_ptrs({q, k, v, o, lse});
+    if (st != FA_OK) return st;
+    fa::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.N = N;
+    fill_scale(scale, a.c2, a.qsign, a.qsign_f);
+    return fa::launch_fwd_bf16(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int attn_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
+                  int d, int causal, float scale, hipStream_t stream) {
+    int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_ptrs({q, k, v, o, lse});
+    if (st != FA_OK) return st;
+    fa::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.N = N;
+    fill_scale(scale, a.c2, a.qsign, a.qsign_f);
+    return fa::launch_fwd_fp32(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_size(int B, int H, int N, int d, int causal) {
+    (void)causal;
+    if (check_shape(B, H, N, d, 1.0f) != FA_OK) return 0;
+    return dd_bytes(B, H, N);
+}
+
+int attn_bwd_prep(const void* o, const void* dO, float* dd, int B, int H, int N, int d, hipStream_t stream) {
+    int st = check_shape(B, H, N, d, 1.0f);
+    if (st != FA_OK) return st;
+    st = check_ptrs({o, dO, dd});
+    if (st != FA_OK) return st;
+    fa::BwdArgs a{};
+    a.o = o; a.dO = dO; a.dd = dd;
+    a.B = B; a.H = H; a.N = N;
+    return fa::launch_bwd_prep(a, d, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+namespace {
+
+int fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* dO, const float* lse,
+             const float* dd, int B, int H, int N, int d, float scale) {
+    int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_ptrs({q, k, v, dO, lse, dd});
+    if (st != FA_OK) return st;
+    a.q = q; a.k = k; a.v = v; a.dO = dO; a.lse = lse;
+    a.dd = const_cast<float*>(dd);
+    a.B = B; a.H = H; a.N = N;
+    a.scale = scale;
+    float unused;
+    fill_scale(scale, a.c2, a.qsign, unused);
+    return FA_OK;
+}
+
+}  // namespace
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* dd,
+                  void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+    fa::BwdArgs a{};
+    int st = fill_bwd(a, q, k, v, dO, lse, dd, B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_ptrs({dk, dv});
+    if (st != FA_OK) return st;
+    a.dk = dk; a.dv = dv;
+    return fa::launch_bwd_dkdv(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* dd,
+                void* dq, int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+    fa::BwdArgs a{};
+    int st = fill_bwd(a, q, k, v, dO, lse, dd, B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_ptrs({dq});
+    if (st != FA_OK) return st;
+    a.dq = dq;
+    return fa::launch_bwd_dq(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+             int causal, float scale, hipStream_t stream) {
+    int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_ptrs({q, k, v, o, dO, lse, dq, dk, dv});
+    if (st != FA_OK) return st;
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < dd_bytes(B, H, N))
+        return FA_ERR_WORKSPACE;
+    float* dd = static_cast<float*>(workspace);
+    st = attn_bwd_prep(o, dO, dd, B, H, N, d, stream);
+    if (st != FA_OK) return st;
+    st = attn_bwd_dkdv(q, k, v, dO, lse, dd, dk, dv, B, H, N, d, causal, scale, stream);
+    if (st != FA_OK) return st;
+    return attn_bwd_dq(q, k, v, dO, lse, dd, dq, B, H, N, d, causal, scale, stream);
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+        default: return "FA_ERR_UNKNOWN";
+    }
+}
+
+}  // extern "C"

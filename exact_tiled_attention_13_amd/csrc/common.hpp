@@ -1,0 +1,125 @@
+// common.hpp -- shared device helpers of libfa_mi355x (gfx950 only).
+//
+// Vector types for the CDNA4 matrix-core builtins, the launch-argument
+// structs, the workgroup -> (tile, head, batch) map and small lane helpers.
+// Every kernel in this library includes this header; nothing here is used by
+// the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Launch arguments of the forward kernels. Tensors are [B, N, H, d] with d
+// fastest; lse is [B, H, N].
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, N;
+    float c2;         // |scale| * log2(e): scores are exponentiated in base 2
+    uint32_t qsign;   // 0x80008000 when scale < 0 (folded into Q's sign bits), else 0
+    float qsign_f;    // -1.0f when scale < 0, else 1.0f (fp32 kernels)
+};
+
+// Launch arguments of the backward kernels.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dO;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dd;        // workspace: D_i = dO_i . O_i, fp32 [B, H, N]
+    int B, H, N;
+    float scale;      // the caller's scale (multiplies dQ and dK)
+    float c2;         // |scale| * log2(e)
+    uint32_t qsign;   // as in FwdArgs
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Remap the dispatch index so that XCD x receives a contiguous range of
+// logical tile indices: the query blocks of one head then run on one XCD at
+// the same time and share that head's K/V tiles in its L2. Bijective on
+// [0, total).
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+    constexpr int kXcd = 8;
+    const int per = total / kXcd;
+    const int rem = total % kXcd;
+    const int x = id % kXcd;
+    const int k = id / kXcd;
+    return x * per + (x < rem ? x : rem) + k;
+}
+
+// Combine a per-lane value with the one held by lane (lane ^ 32): in the
+// 32x32 accumulator layout the two halves of a wave64 hold the same column.
+__device__ __forceinline__ float max_halves(float x) {
+    return __builtin_fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+    return x + __shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even fp32 pair -> packed bf16 pair (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 16-byte global load / store helpers on raw bf16 bits.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Transpose four 8-element bf16 rows (keys r0..r3, 8 consecutive d each) into
+// eight 4-element columns: out[c] holds (r0[c], r1[c], r2[c], r3[c]) as two
+// dwords, for c = 0..7.
+__device__ __forceinline__ void transpose_4x8(const u32x4 (&r)[4], u32x2 (&out)[8]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t a = r[0][w], b = r[1][w], c = r[2][w], d = r[3][w];
+        // even element (low halves), odd element (high halves)
+        out[2 * w][0] = (a & 0xffffu) | (b << 16);
+        out[2 * w][1] = (c & 0xffffu) | (d << 16);
+        out[2 * w + 1][0] = (a >> 16) | (b & 0xffff0000u);
+        out[2 * w + 1][1] = (c >> 16) | (d & 0xffff0000u);
+    }
+}
+
+// Position of tile-local key k inside a V^T / K^T row. Within each 16-key
+// chunk the keys are stored as [0-3, 8-11, 4-7, 12-15] so that the 8 keys
+// one lane half contributes to a 32x32x16 MFMA (keys 4h..4h+3 and
+// 8+4h..8+4h+3, the order a 32x32 accumulator holds them in) are one
+// contiguous 16-byte read. k must be a multiple of 4; returns the position of
+// the group k..k+3.
+__device__ __forceinline__ int kperm4(int k) {
+    const int g = (k >> 2) & 3;
+    return (k & ~15) + ((g & 1) << 3) + ((g >> 1) << 2);
+}
+
+}  // namespace fa

@@ -1,0 +1,255 @@
+// fwd_bf16.hip -- bf16 forward of exact tiled attention for gfx950.
+//
+// Method (page "FlashAttention-2: atención eficiente en GPU para contextos
+// largos"):
+//   * section "Bloques pequeños, normalización global": K/V are streamed in
+//     tiles through on-chip memory (LDS) and an online softmax keeps a running
+//     row maximum m and row sum l, rescaling the partial output, so the N x N
+//     score and probability matrices never reach HBM;
+//   * section "Tres mejoras en la utilización de la GPU": the grid covers
+//     (query block, head, batch), so a single long sequence still fills the
+//     chip; each wavefront owns its own 32 query rows and all four wavefronts
+//     of a workgroup share the K/V tiles in LDS, so no partial output is ever
+//     exchanged between wavefronts; tiles entirely above the causal diagonal
+//     are never loaded, masking runs only on diagonal and ragged-tail tiles,
+//     and the division by the row sum happens once, at the end.
+//
+// CDNA4 mapping (one wavefront = 64 lanes, 32 query rows):
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K tile rows from LDS,
+//                 B = Q^T held in VGPRs for the whole kernel. In the 32x32
+//                 accumulator each lane holds one query column (lane % 32) and
+//                 16 keys, so the row max / row sum are in-lane plus one
+//                 exchange with lane ^ 32.
+//   O^T += V^T P^T  A = V^T tile from LDS (stored transposed, keys permuted
+//                 within 16-key chunks to the order the accumulator holds
+//                 them in), B = P^T converted in registers from the S^T
+//                 accumulator. The O^T accumulator again has one query per
+//                 lane, so the online-softmax rescale is a per-lane scalar.
+//   Softmax in base 2: p = exp2(S * c2 - m) with c2 = |scale| * log2(e); a
+//   negative scale is folded into the sign bits of Q.
+//   K/V tiles are double-buffered in LDS: tile t+1 is fetched from HBM into
+//   registers (16-byte loads) while tile t is multiplied, then written to the
+//   other LDS buffer; one barrier per tile.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace fa {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
+    constexpr int BM = 128;             // query rows per workgroup (4 waves x 32)
+    constexpr int BN = 8192 / D;        // keys per tile: 64 (d=128) or 128 (d=64)
+    constexpr int KS = D + 8;           // K tile row stride in elements (16-byte pad)
+    constexpr int VS = BN + 8;          // V^T tile row stride in elements (16-byte pad)
+    constexpr int K_ELEMS = BN * KS;
+    constexpr int V_ELEMS = D * VS;
+    constexpr int STAGE = K_ELEMS + V_ELEMS;
+    constexpr int NKG = BN / 4;         // V staging: key groups of 4
+    constexpr int DC = D / 16;          // 16-wide d chunks (MFMA K steps of S)
+    constexpr int KB = BN / 32;         // 32-key blocks per tile
+    constexpr int DB = D / 32;          // 32-wide d blocks of O^T
+    static_assert(NKG * (D / 8) == 256, "V staging assumes 256 threads x (4 keys x 8 d)");
+
+    __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
+
+    const int B = a.B, H = a.H, N = a.N;
+    const int nq = (N + BM - 1) / BM;
+    const int r = xcd_remap(blockIdx.x, nq * B * H);
+    const int bh = r / nq;
+    int qb = r - bh * nq;
+    if (CAUSAL) qb = nq - 1 - qb;       // longest rows first
+    const int b = bh / H, h = bh - b * H;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const size_t rs = (size_t)H * D;                       // row stride (elements)
+    const size_t base = ((size_t)b * N * H + h) * D;       // (b, 0, h, 0)
+    const __bf16* Qg = static_cast<const __bf16*>(a.q) + base;
+    const __bf16* Kg = static_cast<const __bf16*>(a.k) + base;
+    const __bf16* Vg = static_cast<const __bf16*>(a.v) + base;
+    __bf16* Og = static_cast<__bf16*>(a.o) + base;
+
+    const int q0 = qb * BM;
+    const int qw = q0 + wave * 32;      // first query row of this wave
+    const int myq = qw + l32;           // query row owned by this lane
+
+    // Q^T fragments (B operand): lane holds Q[myq][c*16 + hi*8 .. +8].
+    bf16x8 qf[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (myq < N) v = ld16(Qg + (size_t)myq * rs + c * 16 + hi * 8);
+        v ^= a.qsign;
+        qf[c] = as_bf16x8(v);
+    }
+
+    const int kend = CAUSAL ? min(N, q0 + BM) : N;
+    const int ntiles = (kend + BN - 1) / BN;
+
+    // Staging registers for one K tile and one V tile (4 x 16 bytes each).
+    u32x4 kr[4], vr[4];
+    const int vkg = tid % NKG;          // V: key group (4 keys)
+    const int vdg = tid / NKG;          // V: d group (8 values)
+
+    auto load_tile = [&](int t) {
+        const int j0 = t * BN;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int id = i * 256 + tid;
+            const int row = id / (D / 8), col = id % (D / 8);
+            const int key = j0 + row;
+            kr[i] = (key < N) ? ld16(Kg + (size_t)key * rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
+            const int vkey = j0 + vkg * 4 + i;
+            vr[i] = (vkey < N) ? ld16(Vg + (size_t)vkey * rs + vdg * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_tile = [&](int stage) {
+        __bf16* Ks = smem + stage * STAGE;
+        __bf16* Vs = Ks + K_ELEMS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int id = i * 256 + tid;
+            const int row = id / (D / 8), col = id % (D / 8);
+            st16(Ks + row * KS + col * 8, kr[i]);
+        }
+        u32x2 cols[8];
+        transpose_4x8(vr, cols);
+        const int pos = kperm4(vkg * 4);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st8(Vs + (vdg * 8 + c) * VS + pos, cols[c]);
+    };
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+    float m = -INFINITY;   // running max of S * c2 (base-2 units) for query myq
+    float l = 0.f;         // running sum over this lane's keys (other half added at the end)
+    const float c2 = a.c2;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = t * BN;
+        if (t + 1 < ntiles) load_tile(t + 1);
+        const __bf16* Ks = smem + (t & 1) * STAGE;
+        const __bf16* Vs = Ks + K_ELEMS;
+
+        // Causal: a wave whose last query precedes the tile's first key sees nothing in it.
+        const bool active = !CAUSAL || (j0 <= qw + 31);
+        if (active) {
+            f32x16 s[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                s[kb] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < DC; ++c) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * KS + c * 16 + hi * 8);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+                }
+            }
+
+            const bool masked = (CAUSAL && j0 + BN - 1 > qw) || (j0 + BN > N);
+            float mx = -INFINITY;
+            uint32_t dead[KB];  // bit u set: element u of block kb is masked
+            if (masked) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    dead[kb] = 0u;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        const int key = j0 + kb * 32 + 8 * (u >> 2) + 4 * hi + (u & 3);
+                        const bool kill = key >= N || (CAUSAL && key > myq);
+                        dead[kb] |= (kill ? 1u : 0u) << u;
+                        if (!kill) mx = __builtin_fmaxf(mx, s[kb][u]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) mx = __builtin_fmaxf(mx, s[kb][u]);
+            }
+            mx = max_halves(mx);
+            const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+            const float mnew = __builtin_fmaxf(m, mt);
+            const float alpha = exp2_fast(m - mnew);
+            m = mnew;
+
+            // P^T as bf16 B operands: pb[kc] covers keys kc*16 .. kc*16+15 of the tile.
+            bf16x8 pb[BN / 16];
+            float rowsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                float p[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    p[u] = exp2_fast(__builtin_fmaf(s[kb][u], c2, -mnew));
+                    if (masked) p[u] = ((dead[kb] >> u) & 1u) ? 0.f : p[u];
+                    rowsum += p[u];
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    u32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[half * 8 + 2 * e], p[half * 8 + 2 * e + 1]);
+                    pb[kb * 2 + half] = as_bf16x8(w);
+                }
+            }
+            l = l * alpha + rowsum;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int kc = 0; kc < BN / 16; ++kc) {
+                    const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (db * 32 + l32) * VS + kc * 16 + hi * 8);
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kc], oacc[db], 0, 0, 0);
+                }
+            }
+        }
+
+        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        __syncthreads();
+    }
+
+    // Epilogue: O = O^T / l (rounded to bf16), LSE = ln-domain m + ln l.
+    const float lt = sum_halves(l);
+    const float inv = 1.0f / lt;
+    if (myq < N) {
+        __bf16* orow = Og + (size_t)myq * rs;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + 8 * g + 4 * hi;
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                st8(orow + d0, w);
+            }
+        }
+        if (hi == 0) a.lse[(size_t)bh * N + myq] = (m + __builtin_log2f(lt)) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+    const int nq = (a.N + 127) / 128;
+    const long long grid = (long long)nq * a.B * a.H;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+    if (d == 128) return causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+    return causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,150 @@
+/*
+ * fa_mi355x.h -- C ABI of libfa_mi355x: exact tiled softmax attention
+ * (forward and backward) for AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * What is computed. Exact softmax attention, per batch b and head h,
+ *
+ *     O = softmax(scale * Q K^T + causal mask) V,    LSE_i = ln sum_j exp(S_ij)
+ *
+ * tile by tile with an online softmax: the kernels keep a running row
+ * maximum and row sum and rescale the partial output, so the N x N score and
+ * probability matrices never reach device memory. Sources, cited by page
+ * title and section:
+ *   - "FlashAttention-2: atención eficiente en GPU para contextos largos",
+ *     section "El coste de mover datos en secuencias largas": the
+ *     conventional computation writes the full score and probability
+ *     matrices to high-bandwidth memory, which is the cost avoided here;
+ *   - same page, section "Bloques pequeños, normalización global": blocks are
+ *     processed in fast on-chip memory and the online softmax rescales the
+ *     running statistics and partial outputs; results equal exact attention
+ *     up to floating-point ordering, and outputs and gradients are compared
+ *     within a tolerance, not bit for bit;
+ *   - same page, section "Tres mejoras en la utilización de la GPU": work is
+ *     split over the sequence as well as batch and heads, query rows are
+ *     split across wavefronts that share the K and V tiles, and non-matrix
+ *     work (rescaling, boundary and causal-mask handling) is kept out of the
+ *     inner loop;
+ *   - "读懂FlashAttention-2：让长上下文注意力更高效地运行在GPU上", section
+ *     "分块处理仍需保持全局归一化": the method is exact attention, not a sparse
+ *     approximation.
+ * The pages do not describe the backward algorithm; attn_bwd computes the
+ * textbook gradients of the definition above (see attn_bwd).
+ *
+ * Conventions shared by every entry point.
+ *   Layout   q, k, v, o, dO, dq, dk, dv are contiguous [B, N, H, d] tensors,
+ *            d fastest (element (b, n, h, c) at ((b*N + n)*H + h)*d + c).
+ *            lse is a contiguous fp32 [B, H, N] tensor, natural log.
+ *   Types    attn_fwd / attn_bwd take raw bfloat16 bits (2 bytes per
+ *            element); attn_fwd_fp32 takes IEEE fp32. Accumulation and all
+ *            softmax statistics are fp32.
+ *   Causal   causal != 0 masks key j for query i when j > i (query and key
+ *            sequences have the same length N).
+ *   Scale    any finite float; it multiplies Q K^T before masking.
+ *   Sizes    B, H, N >= 1; d in {64, 128}; N * H * d < 2^31 and
+ *            B * N * H * d < 2^40.
+ *   Pointers device pointers (hipMalloc'd or equivalent), 16-byte aligned.
+ *   Memory   the caller owns and allocates every buffer, workspace included,
+ *            and the stream. The library never allocates, frees or
+ *            synchronises. Inputs are read-only; outputs are fully
+ *            overwritten and must not alias any input.
+ *   Stream   work is enqueued on `stream` (NULL = the null stream) and the
+ *            call returns without waiting. Faults inside a kernel surface at
+ *            the caller's next synchronisation on that stream.
+ *   Errors   every argument is validated before any HIP call, so a rejected
+ *            call has no side effect. NaN or Inf inside the tensors are not
+ *            checked and propagate.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-valued entry point. */
+enum fa_status {
+    FA_OK = 0,               /* work enqueued */
+    FA_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, size <= 0 or too large, non-finite scale */
+    FA_ERR_UNSUPPORTED = 2,  /* head dimension d not in {64, 128} */
+    FA_ERR_WORKSPACE = 3,    /* workspace null or smaller than attn_bwd_workspace_size() */
+    FA_ERR_HIP = 4           /* a HIP launch reported an error (hipGetLastError) */
+};
+
+/*
+ * attn_fwd -- bf16 forward of exact attention (definition above).
+ *   q, k, v  [B, N, H, d] bf16 inputs.
+ *   o        [B, N, H, d] bf16 output, rounded to nearest even from fp32.
+ *   lse      [B, H, N] fp32 output: natural-log log-sum-exp of row i of the
+ *            scaled, masked scores (the statistic attn_bwd consumes).
+ * The online softmax runs in fp32 (base-2 internally); the probabilities fed
+ * to the second product are rounded to bf16, the row sum uses them unrounded.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_fwd_fp32 -- the same forward with fp32 inputs, outputs and products
+ * (no value is rounded below fp32). Arguments as for attn_fwd.
+ */
+int attn_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
+                  int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for this
+ * shape (the per-row statistic D_i = dO_i . O_i, fp32 [B, H, N], rounded up to
+ * 256 bytes). Returns 0 for arguments attn_bwd would reject.
+ */
+size_t attn_bwd_workspace_size(int B, int H, int N, int d, int causal);
+
+/*
+ * attn_bwd -- bf16 gradients of exact attention with respect to q, k, v.
+ *   q, k, v  forward inputs, [B, N, H, d] bf16.
+ *   o, lse   the forward's outputs for these inputs (from attn_fwd).
+ *   dO       upstream gradient dL/dO, [B, N, H, d] bf16.
+ *   dq,dk,dv outputs, [B, N, H, d] bf16 (rounded to nearest even from fp32).
+ *   workspace, workspace_bytes: caller-owned device scratch of at least
+ *            attn_bwd_workspace_size(B, H, N, d, causal) bytes, 256-byte
+ *            aligned; its contents on entry are ignored and on return are
+ *            unspecified.
+ * Gradients (chain rule through the row softmax; P is recomputed from q, k
+ * and lse, never stored):
+ *     D_i = dO_i . O_i,  dP = dO V^T,  dS = P o (dP - D),
+ *     dV = P^T dO,  dQ = scale * dS K,  dK = scale * dS^T Q.
+ * The result is deterministic: no atomics; repeated calls give identical bits.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes,
+             int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * The three stages attn_bwd runs, in order, on one stream. They are exported
+ * so that a caller can time or schedule them separately; attn_bwd is exactly
+ * attn_bwd_prep, then attn_bwd_dkdv, then attn_bwd_dq with dd = workspace.
+ *
+ * attn_bwd_prep -- dd[b, h, i] = sum_c dO[b, i, h, c] * O[b, i, h, c] in fp32
+ *   (the row statistic D_i = sum_j P_ij dP_ij of the softmax backward).
+ *   o, dO: [B, N, H, d] bf16 inputs; dd: fp32 [B, H, N] output.
+ * attn_bwd_dkdv -- dk = scale * dS^T Q and dv = P^T dO, one workgroup per
+ *   block of 128 keys looping over query tiles; reads dd from attn_bwd_prep.
+ * attn_bwd_dq -- dq = scale * dS K, one workgroup per block of 128 queries
+ *   looping over key tiles (recomputes P and dP); reads dd.
+ * Arguments and errors as for attn_bwd; dd must be 16-byte aligned.
+ */
+int attn_bwd_prep(const void* o, const void* dO, float* dd, int B, int H, int N, int d, hipStream_t stream);
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* dd,
+                  void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* dd,
+                void* dq, int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/* fa_status_string -- static, human-readable name of a status code. Never NULL. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

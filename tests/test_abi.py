@@ -1,0 +1,92 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/fa_mi355x.h, and rejects bad arguments before any HIP call.
+
+Every call made here fails validation, so no kernel is launched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_13_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+# Fake device addresses: non-null and 16-byte aligned (never dereferenced).
+P = 0x100000
+MIS = 0x100008  # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert fa.status_string(0) == "FA_OK"
+    assert fa.status_string(1) == "FA_ERR_INVALID_ARG"
+    assert fa.status_string(2) == "FA_ERR_UNSUPPORTED"
+    assert fa.status_string(3) == "FA_ERR_WORKSPACE"
+    assert fa.status_string(4) == "FA_ERR_HIP"
+    assert fa.status_string(99) == "FA_ERR_UNKNOWN"
+
+
+def fwd(fn="attn_fwd", q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, causal=0, scale=0.125):
+    return getattr(fa.lib(), fn)(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_fp32"])
+def test_forward_rejects_bad_arguments(fn):
+    assert fwd(fn, q=0) == fa.FA_ERR_INVALID_ARG
+    assert fwd(fn, lse=0) == fa.FA_ERR_INVALID_ARG
+    assert fwd(fn, o=MIS) == fa.FA_ERR_INVALID_ARG
+    assert fwd(fn, q=P, B=0) == fa.FA_ERR_INVALID_ARG
+    assert fwd(fn, H=-1) == fa.FA_ERR_INVALID_ARG
+    assert fwd(fn, N=0) == fa.FA_ERR_INVALID_ARG
+    assert fwd(fn, scale=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert fwd(fn, scale=float("inf")) == fa.FA_ERR_INVALID_ARG
+    assert fwd(fn, N=1 << 24, H=1024, d=128) == fa.FA_ERR_INVALID_ARG  # N*H*d >= 2^31
+    for d in (0, 32, 96, 256):
+        assert fwd(fn, d=d) == fa.FA_ERR_UNSUPPORTED
+    # Size checks come before pointer checks: a bad size with a null pointer is still INVALID_ARG.
+    assert fwd(fn, q=0, d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+def bwd(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, ws_bytes=1 << 20, B=1, H=1, N=16, d=64,
+        causal=0, scale=0.125):
+    return fa.lib().attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, N, d, causal, scale, None)
+
+
+def test_backward_rejects_bad_arguments():
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert bwd(**{name: 0}) == fa.FA_ERR_INVALID_ARG, name
+        assert bwd(**{name: MIS}) == fa.FA_ERR_INVALID_ARG, name
+    assert bwd(B=0) == fa.FA_ERR_INVALID_ARG
+    assert bwd(scale=float("-inf")) == fa.FA_ERR_INVALID_ARG
+    assert bwd(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(ws=0) == fa.FA_ERR_WORKSPACE
+    assert bwd(ws=MIS) == fa.FA_ERR_WORKSPACE
+    need = fa.attn_bwd_workspace_size(1, 1, 16, 64, False)
+    assert bwd(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+
+
+def test_workspace_size():
+    assert fa.attn_bwd_workspace_size(1, 1, 16, 64, False) == 256
+    assert fa.attn_bwd_workspace_size(4, 16, 4096, 128, True) == 4 * 16 * 4096 * 4
+    assert fa.attn_bwd_workspace_size(1, 1, 65, 64, False) == 512  # 260 bytes rounded up to 256
+    assert fa.attn_bwd_workspace_size(0, 1, 16, 64, False) == 0
+    assert fa.attn_bwd_workspace_size(1, 1, 16, 96, False) == 0

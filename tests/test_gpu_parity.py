@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Every case draws seeded inputs once on the CPU (exact_tiled_attention_13_amd.inputs),
+runs the library on cuda:0 and the oracle on the identical values, and
+compares with the tolerances in parity_util. Small and medium shapes are
+compared element by element over whole tensors, with sizes that span several
+tiles and a ragged tail; the full-size workloads are compared on sampled
+heads and rows the oracle can compute one by one, in the same launch
+configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_13_amd as fa
+from exact_tiled_attention_13_amd.inputs import WORKLOADS, make_qkv, make_workload
+from oracle import attn_bwd_head, attn_fwd, attn_fwd_rows, attn_bwd
+from parity_util import (DEV, TOL_GRAD_BF16, TOL_LSE_BF16, TOL_LSE_FP32, TOL_O_BF16, TOL_O_FP32, aerr, f64,
+                         nerr, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(q, k, v, causal, scale, fp32=False):
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = (fa.attn_fwd_fp32 if fp32 else fa.attn_fwd)(qd, kd, vd, causal, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# fp32 forward
+
+def test_fwd_fp32_workload():
+    w = WORKLOADS["fwd_fp32_b1_h2_n128_d64"]
+    q, k, v = make_workload(w)
+    o, lse = run_fwd(q, k, v, False, w.scale, fp32=True)
+    ro, rl = attn_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), False, w.scale)
+    assert nerr(f64(o), ro) <= TOL_O_FP32
+    assert aerr(f64(lse), rl) <= TOL_LSE_FP32
+
+
+@pytest.mark.parametrize("N", [1, 17, 100, 257, 600])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp32_shapes(N, d, causal):
+    q, k, v = make_qkv(2, 3, N, d, "fp32", seed=N * 10 + d + causal)
+    s = float(np.float32(d ** -0.5))
+    o, lse = run_fwd(q, k, v, causal, s, fp32=True)
+    ro, rl = attn_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, s)
+    assert nerr(f64(o), ro) <= TOL_O_FP32
+    assert aerr(f64(lse), rl) <= TOL_LSE_FP32
+
+
+# ---------------------------------------------------------------------------
+# bf16 forward, whole-tensor comparison
+
+@pytest.mark.parametrize("N", [1, 17, 100, 129, 257, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_bf16_shapes(N, d, causal):
+    q, k, v = make_qkv(2, 3, N, d, "bf16", seed=N * 10 + d + causal + 7)
+    s = float(np.float32(d ** -0.5))
+    o, lse = run_fwd(q, k, v, causal, s)
+    ro, rl = attn_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, s)
+    assert nerr(f64(o), ro) <= TOL_O_BF16
+    assert aerr(f64(lse), rl) <= TOL_LSE_BF16
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_bf16_other_scales(scale, causal):
+    q, k, v = make_qkv(1, 2, 300, 64, "bf16", seed=55)
+    o, lse = run_fwd(q, k, v, causal, scale)
+    ro, rl = attn_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, scale)
+    assert nerr(f64(o), ro) <= TOL_O_BF16
+    assert aerr(f64(lse), rl) <= TOL_LSE_BF16
+
+
+def test_fwd_bf16_workload_n512_d64():
+    """32 batches x 32 heads x 512 tokens, d 64, both masks: whole tensors."""
+    w = WORKLOADS["fwd_bf16_b32_h32_n512_d64"]
+    q, k, v = make_workload(w)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    for causal in w.causal:
+        o, lse = run_fwd(q, k, v, causal, w.scale)
+        ro, rl = attn_fwd(qn, kn, vn, causal, w.scale)
+        assert nerr(f64(o), ro) <= TOL_O_BF16, causal
+        assert aerr(f64(lse), rl) <= TOL_LSE_BF16, causal
+
+
+def sampled_fwd_check(w, heads, nrows):
+    q, k, v = make_workload(w)
+    for causal in w.causal:
+        o, lse = run_fwd(q, k, v, causal, w.scale)
+        o, lse = o.cpu(), lse.cpu()
+        got_o, ref_o, got_l, ref_l = [], [], [], []
+        for i, (b, h) in enumerate(heads):
+            rows = sample_rows(w.N, nrows, seed=w.seed + i)
+            ro, rl = attn_fwd_rows(q[b, :, h].double().numpy(), k[b, :, h].double().numpy(),
+                                   v[b, :, h].double().numpy(), rows, causal, w.scale)
+            got_o.append(f64(o[b, rows, h]))
+            ref_o.append(ro)
+            got_l.append(f64(lse[b, h, rows]))
+            ref_l.append(rl)
+        assert nerr(np.concatenate(got_o), np.concatenate(ref_o)) <= TOL_O_BF16, causal
+        assert aerr(np.concatenate(got_l), np.concatenate(ref_l)) <= TOL_LSE_BF16, causal
+
+
+def test_fwd_bf16_workload_n2048_d128_sampled():
+    w = WORKLOADS["fwd_bf16_b8_h16_n2048_d128"]
+    sampled_fwd_check(w, heads=[(0, 0), (3, 7), (7, 15)], nrows=256)
+
+
+def test_fwd_bf16_workload_n16384_d128_sampled():
+    w = WORKLOADS["fwd_bf16_b1_h16_n16384_d128"]
+    sampled_fwd_check(w, heads=[(0, 0), (0, 9), (0, 15)], nrows=192)
+
+
+# ---------------------------------------------------------------------------
+# bf16 backward
+
+def run_bwd(q, k, v, do, causal, scale):
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa.attn_fwd(qd, kd, vd, causal, scale)
+    dq, dk, dv = fa.attn_bwd(qd, kd, vd, o, dod, lse, causal, scale)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("N", [1, 17, 100, 257, 640])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_bf16_shapes(N, d, causal):
+    q, k, v, do = make_qkv(2, 2, N, d, "bf16", seed=N * 3 + d + causal, with_do=True)
+    s = float(np.float32(d ** -0.5))
+    _, _, dq, dk, dv = run_bwd(q, k, v, do, causal, s)
+    rq, rk, rv = attn_bwd(*(x.double().numpy() for x in (q, k, v, do)), causal, s)
+    assert nerr(f64(dq), rq) <= TOL_GRAD_BF16
+    assert nerr(f64(dk), rk) <= TOL_GRAD_BF16
+    assert nerr(f64(dv), rv) <= TOL_GRAD_BF16
+
+
+@pytest.mark.parametrize("scale", [-0.15, 0.0])
+def test_bwd_bf16_other_scales(scale):
+    q, k, v, do = make_qkv(1, 2, 200, 128, "bf16", seed=66, with_do=True)
+    for causal in (False, True):
+        _, _, dq, dk, dv = run_bwd(q, k, v, do, causal, scale)
+        rq, rk, rv = attn_bwd(*(x.double().numpy() for x in (q, k, v, do)), causal, scale)
+        assert nerr(f64(dq), rq) <= TOL_GRAD_BF16
+        assert nerr(f64(dk), rk) <= TOL_GRAD_BF16
+        assert nerr(f64(dv), rv) <= TOL_GRAD_BF16
+
+
+def test_bwd_bf16_workload_n4096_sampled_heads():
+    """4 x 16 heads x 4096 tokens, d 128, causal: O and LSE from the forward
+    kernel feed the backward; three whole heads are checked against the oracle."""
+    w = WORKLOADS["bwd_bf16_b4_h16_n4096_d128"]
+    q, k, v, do = make_workload(w)
+    causal = True
+    o, lse, dq, dk, dv = (t.cpu() for t in run_bwd(q, k, v, do, causal, w.scale))
+    got = {"o": [], "dq": [], "dk": [], "dv": []}
+    ref = {"o": [], "dq": [], "dk": [], "dv": []}
+    for b, h in [(0, 0), (2, 5), (3, 15)]:
+        g = attn_bwd_head(*(x[b, :, h].double().numpy() for x in (q, k, v, do)), causal, w.scale)
+        for name, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+            got[name].append(f64(t[b, :, h]))
+            ref[name].append(g[name])
+        assert aerr(f64(lse[b, h]), g["lse"]) <= TOL_LSE_BF16
+    assert nerr(np.concatenate(got["o"]), np.concatenate(ref["o"])) <= TOL_O_BF16
+    for name in ("dq", "dk", "dv"):
+        assert nerr(np.concatenate(got[name]), np.concatenate(ref[name])) <= TOL_GRAD_BF16, name
