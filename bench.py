@@ -37,34 +37,33 @@ def counted_fwd(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
-def cpu_baseline(q, k, v, do, scale):
-    """Time the fp64 oracle on a bounded sample of the workload (rank 0 only)."""
-    import numpy as np
+def cpu_baseline(q, k, v, do, scale, heads=2):
+    """Time the fp64 oracle on a bounded sample of the step: the whole step
+    (forward and backward, both masks) for the first `heads` heads."""
     from threadpoolctl import threadpool_info
 
-    from oracle import attn_bwd_head, attn_fwd_rows
+    from oracle import attn_bwd_head
 
     B, N, H, d = q.shape
-    rows = np.arange(0, N, N // 2048)[:2048]
-    qh, kh, vh = (x[0, :, 0].double().numpy() for x in (q, k, v))
-    nb = 4096
-    qb, kb, vb, gb = (x[0, :nb, 1].double().numpy() for x in (q, k, v, do))
     t0 = time.perf_counter()
-    attn_fwd_rows(qh, kh, vh, rows, False, scale)
+    flops = 0.0
+    for h in range(heads):
+        qh, kh, vh, gh = (x[0, :, h].double().numpy() for x in (q, k, v, do))
+        for causal in (False, True):
+            # attn_bwd_head runs the oracle forward (O, LSE) and the backward.
+            attn_bwd_head(qh, kh, vh, gh, causal, scale)
+            flops += 3.5 * counted_fwd(1, 1, N, d, causal)
     t1 = time.perf_counter()
-    attn_bwd_head(qb, kb, vb, gb, False, scale)
-    t2 = time.perf_counter()
-    flops = 4.0 * len(rows) * N * d + 2.5 * counted_fwd(1, 1, nb, d, False)
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     return {
-        "value": flops / (t2 - t0) / 1e12,
+        "value": flops / (t1 - t0) / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: forward of {len(rows)} query rows x {N} keys of one head "
-                   f"(non-causal, {t1 - t0:.2f} s) plus the full backward of one head truncated to its first "
-                   f"{nb} tokens ({t2 - t1:.2f} s); same inputs and counted-FLOP formula as the GPU step"),
-        "seconds": t2 - t0,
+        "sample": (f"fp64 numpy oracle running the whole step (forward and backward, non-causal and causal) "
+                   f"for {heads} of the {H} heads of the same inputs, {t1 - t0:.1f} s; value uses the "
+                   f"same counted-FLOP formula as the GPU step"),
+        "seconds": round(t1 - t0, 2),
     }
 
 
