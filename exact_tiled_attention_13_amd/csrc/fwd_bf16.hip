@@ -35,9 +35,17 @@
 
 namespace fa {
 
+// Online-softmax bookkeeping: the running maximum m is only moved when a
+// tile's maximum exceeds it by more than kTau (base-2 units). Between moves the
+// exponentials are taken against the stale m, so they stay below 2^kTau, and
+// the final O / l and LSE = m + log2(l) are unchanged: the result is the same
+// exact softmax, with the rescale of l and O skipped for most tiles.
+constexpr float kTau = 8.0f;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
-    constexpr int BM = 128;             // query rows per workgroup (4 waves x 32)
+__global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
+    constexpr int NW = 8;               // waves per workgroup (2 per SIMD)
+    constexpr int BM = NW * 32;         // query rows per workgroup
     constexpr int BN = 8192 / D;        // keys per tile: 64 (d=128) or 128 (d=64)
     constexpr int KS = D + 8;           // K tile row stride in elements (16-byte pad)
     constexpr int VS = BN + 8;          // V^T tile row stride in elements (16-byte pad)
@@ -90,43 +98,55 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
     const int kend = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kend + BN - 1) / BN;
 
-    // Staging registers for one K tile and one V tile (4 x 16 bytes each).
-    u32x4 kr[4], vr[4];
-    const int vkg = tid % NKG;          // V: key group (4 keys)
-    const int vdg = tid / NKG;          // V: d group (8 values)
+    // Staging: waves 0-3 bring V (4 keys x 8 d per thread, stored transposed),
+    // waves 4-7 bring K (four 16-byte row pieces per thread, stored as is).
+    const bool vstager = tid < 256;
+    const int st = tid & 255;
+    const int vkg = st % NKG;           // V: key group (4 keys)
+    const int vdg = st / NKG;           // V: d group (8 values)
+    u32x4 sr[4];
 
     auto load_tile = [&](int t) {
         const int j0 = t * BN;
+        if (vstager) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = i * 256 + tid;
-            const int row = id / (D / 8), col = id % (D / 8);
-            const int key = j0 + row;
-            kr[i] = (key < N) ? ld16(Kg + (size_t)key * rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
-            const int vkey = j0 + vkg * 4 + i;
-            vr[i] = (vkey < N) ? ld16(Vg + (size_t)vkey * rs + vdg * 8) : u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < 4; ++i) {
+                const int key = j0 + vkg * 4 + i;
+                sr[i] = (key < N) ? ld16(Vg + (size_t)key * rs + vdg * 8) : u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int id = i * 256 + st;
+                const int row = id / (D / 8), col = id % (D / 8);
+                const int key = j0 + row;
+                sr[i] = (key < N) ? ld16(Kg + (size_t)key * rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
+            }
         }
     };
     auto store_tile = [&](int stage) {
         __bf16* Ks = smem + stage * STAGE;
         __bf16* Vs = Ks + K_ELEMS;
+        if (vstager) {
+            u32x2 cols[8];
+            transpose_4x8(sr, cols);
+            const int pos = kperm4(vkg * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = i * 256 + tid;
-            const int row = id / (D / 8), col = id % (D / 8);
-            st16(Ks + row * KS + col * 8, kr[i]);
+            for (int c = 0; c < 8; ++c) st8(Vs + (vdg * 8 + c) * VS + pos, cols[c]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int id = i * 256 + st;
+                const int row = id / (D / 8), col = id % (D / 8);
+                st16(Ks + row * KS + col * 8, sr[i]);
+            }
         }
-        u32x2 cols[8];
-        transpose_4x8(vr, cols);
-        const int pos = kperm4(vkg * 4);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) st8(Vs + (vdg * 8 + c) * VS + pos, cols[c]);
     };
 
     f32x16 oacc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-    float m = -INFINITY;   // running max of S * c2 (base-2 units) for query myq
+    float m = -INFINITY;   // reference max of S * c2 (base-2 units) for query myq
     float l = 0.f;         // running sum over this lane's keys (other half added at the end)
     const float c2 = a.c2;
 
@@ -177,9 +197,14 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
             }
             mx = max_halves(mx);
             const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
-            const float mnew = __builtin_fmaxf(m, mt);
-            const float alpha = exp2_fast(m - mnew);
-            m = mnew;
+            if (__builtin_amdgcn_ballot_w64(mt > m + kTau) != 0) {
+                const float mnew = __builtin_fmaxf(m, mt);
+                const float alpha = exp2_fast(m - mnew);
+                m = mnew;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            }
 
             // P^T as bf16 B operands: pb[kc] covers keys kc*16 .. kc*16+15 of the tile.
             bf16x8 pb[BN / 16];
@@ -189,7 +214,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
                 float p[16];
 #pragma unroll
                 for (int u = 0; u < 16; ++u) {
-                    p[u] = exp2_fast(__builtin_fmaf(s[kb][u], c2, -mnew));
+                    p[u] = exp2_fast(__builtin_fmaf(s[kb][u], c2, -m));
                     if (masked) p[u] = ((dead[kb] >> u) & 1u) ? 0.f : p[u];
                     rowsum += p[u];
                 }
@@ -201,9 +226,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
                     pb[kb * 2 + half] = as_bf16x8(w);
                 }
             }
-            l = l * alpha + rowsum;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            l += rowsum;
 
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -241,9 +264,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    const int nq = (a.N + 127) / 128;
+    const int nq = (a.N + 255) / 256;
     const long long grid = (long long)nq * a.B * a.H;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
