@@ -42,34 +42,40 @@ namespace fa {
 // exact softmax, with the rescale of l and O skipped for most tiles.
 constexpr float kTau = 8.0f;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
-    constexpr int NW = 8;               // waves per workgroup (2 per SIMD)
-    constexpr int BM = NW * 32;         // query rows per workgroup
-    constexpr int BN = 8192 / D;        // keys per tile: 64 (d=128) or 128 (d=64)
-    constexpr int KS = D + 8;           // K tile row stride in elements (16-byte pad)
-    constexpr int VS = BN + 8;          // V^T tile row stride in elements (16-byte pad)
-    constexpr int K_ELEMS = BN * KS;
-    constexpr int V_ELEMS = D * VS;
-    constexpr int STAGE = K_ELEMS + V_ELEMS;
-    constexpr int NKG = BN / 4;         // V staging: key groups of 4
-    constexpr int DC = D / 16;          // 16-wide d chunks (MFMA K steps of S)
-    constexpr int KB = BN / 32;         // 32-key blocks per tile
-    constexpr int DB = D / 32;          // 32-wide d blocks of O^T
-    static_assert(NKG * (D / 8) == 256, "V staging assumes 256 threads x (4 keys x 8 d)");
+    constexpr int NW = 8;                 // waves per workgroup (2 per SIMD)
+    constexpr int BM = NW * 32;           // query rows per workgroup
+    constexpr int BN = 64;                // keys per tile
+    constexpr int RB = D * 2;             // bytes per K/V row
+    constexpr int TILE = BN * RB;         // bytes per K or V tile
+    constexpr int NINST = TILE / 1024;    // 1 KB direct-to-LDS wave loads per tile
+    constexpr int IPW = NINST / NW;       // ... per wave
+    constexpr int RPI = 1024 / RB;        // rows covered by one such load
+    constexpr int CPR = RB / 16;          // 16-byte chunks per row
+    constexpr int DC = D / 16;            // 16-wide d chunks (MFMA K steps of S)
+    constexpr int KB = BN / 32;           // 32-key blocks per tile
+    constexpr int DB = D / 32;            // 32-wide d blocks of O^T
+    static_assert(IPW * NW == NINST && IPW >= 1, "tile must split evenly over the waves");
 
-    __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
+    // LDS: Kbuf[0], Kbuf[1], Vbuf[0], Vbuf[1]; rows unpadded, 16-byte chunks
+    // XOR-swizzled per row (see swk / swv) so that the MFMA operand reads are
+    // free of bank conflicts.
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];
 
     const int B = a.B, H = a.H, N = a.N;
     const int nq = (N + BM - 1) / BM;
     const int r = xcd_remap(blockIdx.x, nq * B * H);
     const int bh = r / nq;
     int qb = r - bh * nq;
-    if (CAUSAL) qb = nq - 1 - qb;       // longest rows first
+    if (CAUSAL) qb = nq - 1 - qb;         // longest rows first
     const int b = bh / H, h = bh - b * H;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
@@ -82,8 +88,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
     __bf16* Og = static_cast<__bf16*>(a.o) + base;
 
     const int q0 = qb * BM;
-    const int qw = q0 + wave * 32;      // first query row of this wave
-    const int myq = qw + l32;           // query row owned by this lane
+    const int qw = q0 + wave * 32;        // first query row of this wave
+    const int myq = qw + l32;             // query row owned by this lane
 
     // Q^T fragments (B operand): lane holds Q[myq][c*16 + hi*8 .. +8].
     bf16x8 qf[DC];
@@ -98,47 +104,55 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
     const int kend = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kend + BN - 1) / BN;
 
-    // Staging: waves 0-3 bring V (4 keys x 8 d per thread, stored transposed),
-    // waves 4-7 bring K (four 16-byte row pieces per thread, stored as is).
-    const bool vstager = tid < 256;
-    const int st = tid & 255;
-    const int vkg = st % NKG;           // V: key group (4 keys)
-    const int vdg = st / NKG;           // V: d group (8 values)
-    u32x4 sr[4];
+    // Row swizzles of the 16-byte chunks. K rows are read 16 rows at a time at
+    // one chunk column; V rows are read by the transposing loads 4 rows x 64
+    // bytes at a time.
+    auto swk = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+    auto swv = [](int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
 
-    auto load_tile = [&](int t) {
-        const int j0 = t * BN;
-        if (vstager) {
+    // Direct-to-LDS tile load: wave load j covers rows inst*RPI .. +RPI-1 of
+    // the tile; lane i writes LDS chunk slot i, so it fetches the global chunk
+    // that the swizzle puts there. Rows past N are clamped to N-1 (they are
+    // masked for K and meet P = 0 for V).
+    auto dma = [&](const __bf16* g, int t, int buf, bool is_v) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = j0 + vkg * 4 + i;
-                sr[i] = (key < N) ? ld16(Vg + (size_t)key * rs + vdg * 8) : u32x4{0u, 0u, 0u, 0u};
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int id = i * 256 + st;
-                const int row = id / (D / 8), col = id % (D / 8);
-                const int key = j0 + row;
-                sr[i] = (key < N) ? ld16(Kg + (size_t)key * rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int j = 0; j < IPW; ++j) {
+            const int inst = wave + NW * j;
+            const int row = inst * RPI + lane / CPR;
+            const int slot = lane % CPR;
+            const int c = slot ^ (is_v ? swv(row) : swk(row));
+            const int grow = min(t * BN + row, N - 1);
+            __builtin_amdgcn_global_load_lds(g + (size_t)grow * rs + c * 8,
+                                             (lds_void_t*)(smem + buf * TILE + inst * 1024), 16, 0, 0);
         }
     };
-    auto store_tile = [&](int stage) {
-        __bf16* Ks = smem + stage * STAGE;
-        __bf16* Vs = Ks + K_ELEMS;
-        if (vstager) {
-            u32x2 cols[8];
-            transpose_4x8(sr, cols);
-            const int pos = kperm4(vkg * 4);
+    auto kbuf = [&](int i) { return smem + i * TILE; };
+    auto vbuf = [&](int i) { return smem + (2 + i) * TILE; };
+
+    // Per-lane byte offsets of the MFMA operand reads.
+    int koff[DC];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) st8(Vs + (vdg * 8 + c) * VS + pos, cols[c]);
-        } else {
+    for (int cc = 0; cc < DC; ++cc) koff[cc] = l32 * RB + (((2 * cc + hi) ^ swk(l32)) << 4);
+    int voff[DB];
+    {
+        const int g = lane >> 4, i = lane & 15;
+        const int e = i >> 2;                              // key within the group of 4
+        const int x = 2 * (g & 1) + ((i & 3) >> 1);        // chunk within the 64-byte run
+        const int sq = (D == 128 ? e : (e >> 1));          // swizzle of that key row, in quads
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int id = i * 256 + st;
-                const int row = id / (D / 8), col = id % (D / 8);
-                st16(Ks + row * KS + col * 8, sr[i]);
+        for (int db = 0; db < DB; ++db) voff[db] = (4 * hi + e) * RB + ((4 * (db ^ sq) + x) << 4) + ((i & 1) << 3);
+    }
+
+    auto wave_active = [&](int t) { return !CAUSAL || (t * BN <= qw + 31); };
+
+    auto scores = [&](f32x16 (&s)[KB], const unsigned char* Ks) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            s[kb] = f32x16{};
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * RB + koff[cc]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cc], s[kb], 0, 0, 0);
             }
         }
     };
@@ -150,96 +164,105 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
     float l = 0.f;         // running sum over this lane's keys (other half added at the end)
     const float c2 = a.c2;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
+    // softmax of tile t held in s, then O^T += V_t^T P_t^T.
+    auto softmax_pv = [&](int t, f32x16 (&s)[KB]) {
         const int j0 = t * BN;
-        if (t + 1 < ntiles) load_tile(t + 1);
-        const __bf16* Ks = smem + (t & 1) * STAGE;
-        const __bf16* Vs = Ks + K_ELEMS;
-
-        // Causal: a wave whose last query precedes the tile's first key sees nothing in it.
-        const bool active = !CAUSAL || (j0 <= qw + 31);
-        if (active) {
-            f32x16 s[KB];
+        const bool masked = (CAUSAL && j0 + BN - 1 > qw) || (j0 + BN > N);
+        float mx = -INFINITY;
+        uint32_t dead[KB];  // bit u set: element u of block kb is masked
+        if (masked) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                s[kb] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < DC; ++c) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * KS + c * 16 + hi * 8);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
-                }
-            }
-
-            const bool masked = (CAUSAL && j0 + BN - 1 > qw) || (j0 + BN > N);
-            float mx = -INFINITY;
-            uint32_t dead[KB];  // bit u set: element u of block kb is masked
-            if (masked) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    dead[kb] = 0u;
-#pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        const int key = j0 + kb * 32 + 8 * (u >> 2) + 4 * hi + (u & 3);
-                        const bool kill = key >= N || (CAUSAL && key > myq);
-                        dead[kb] |= (kill ? 1u : 0u) << u;
-                        if (!kill) mx = __builtin_fmaxf(mx, s[kb][u]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int u = 0; u < 16; ++u) mx = __builtin_fmaxf(mx, s[kb][u]);
-            }
-            mx = max_halves(mx);
-            const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
-            if (__builtin_amdgcn_ballot_w64(mt > m + kTau) != 0) {
-                const float mnew = __builtin_fmaxf(m, mt);
-                const float alpha = exp2_fast(m - mnew);
-                m = mnew;
-                l *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-            }
-
-            // P^T as bf16 B operands: pb[kc] covers keys kc*16 .. kc*16+15 of the tile.
-            bf16x8 pb[BN / 16];
-            float rowsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                float p[16];
+                dead[kb] = 0u;
 #pragma unroll
                 for (int u = 0; u < 16; ++u) {
-                    p[u] = exp2_fast(__builtin_fmaf(s[kb][u], c2, -m));
-                    if (masked) p[u] = ((dead[kb] >> u) & 1u) ? 0.f : p[u];
-                    rowsum += p[u];
-                }
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    u32x4 w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[half * 8 + 2 * e], p[half * 8 + 2 * e + 1]);
-                    pb[kb * 2 + half] = as_bf16x8(w);
+                    const int key = j0 + kb * 32 + 8 * (u >> 2) + 4 * hi + (u & 3);
+                    const bool kill = key >= N || (CAUSAL && key > myq);
+                    dead[kb] |= (kill ? 1u : 0u) << u;
+                    if (!kill) mx = __builtin_fmaxf(mx, s[kb][u]);
                 }
             }
-            l += rowsum;
-
+        } else {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int kc = 0; kc < BN / 16; ++kc) {
-                    const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (db * 32 + l32) * VS + kc * 16 + hi * 8);
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kc], oacc[db], 0, 0, 0);
-                }
-            }
+                for (int u = 0; u < 16; ++u) mx = __builtin_fmaxf(mx, s[kb][u]);
+        }
+        mx = max_halves(mx);
+        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+        if (__builtin_amdgcn_ballot_w64(mt > m + kTau) != 0) {
+            const float mnew = __builtin_fmaxf(m, mt);
+            const float alpha = exp2_fast(m - mnew);
+            m = mnew;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         }
 
-        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        // P^T as bf16 B operands: pb[kc] covers keys kc*16 .. kc*16+15 of the tile.
+        bf16x8 pb[BN / 16];
+        float rowsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float p[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                p[u] = exp2_fast(__builtin_fmaf(s[kb][u], c2, -m));
+                if (masked) p[u] = ((dead[kb] >> u) & 1u) ? 0.f : p[u];
+                rowsum += p[u];
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[half * 8 + 2 * e], p[half * 8 + 2 * e + 1]);
+                pb[kb * 2 + half] = as_bf16x8(w);
+            }
+        }
+        l += rowsum;
+
+        // V^T operand by transposing LDS reads of the row-major V tile.
+        const unsigned char* Vs = vbuf(t & 1);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int kc = 0; kc < BN / 16; ++kc) {
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16_t*)(Vs + kc * 16 * RB + voff[db]));
+                const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16_t*)(Vs + (kc * 16 + 8) * RB + voff[db]));
+                const v8i16 vv = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[kc],
+                                                                   oacc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+
+    // Prologue: K_0, V_0, K_1 into LDS, then S_0.
+    dma(Kg, 0, 0, false);
+    dma(Vg, 0, 2, true);
+    if (ntiles > 1) dma(Kg, 1, 1, false);
+    wait_dma();
+    __syncthreads();
+    f32x16 sa[KB], sb[KB];
+    scores(sa, kbuf(0));
+    __syncthreads();   // Kbuf[0] receives K_2 in iteration 0
+
+    // One pipeline step: K_{t+2} and V_{t+1} stream into LDS while the scores
+    // of tile t+1 are multiplied and the softmax and PV of tile t run.
+    auto step = [&](int t, f32x16 (&scur)[KB], f32x16 (&snext)[KB]) {
+        if (t + 2 < ntiles) dma(Kg, t + 2, t & 1, false);
+        if (t + 1 < ntiles) dma(Vg, t + 1, 2 + ((t + 1) & 1), true);
+        if (t + 1 < ntiles && wave_active(t + 1)) scores(snext, kbuf((t + 1) & 1));
+        if (wave_active(t)) softmax_pv(t, scur);
+        wait_dma();
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, sa, sb);
+        if (t + 1 < ntiles) step(t + 1, sb, sa);
     }
 
     // Epilogue: O = O^T / l (rounded to bf16), LSE = ln-domain m + ln l.
