@@ -3,6 +3,7 @@
 // Validates every argument before touching HIP, derives the kernel
 // constants (base-2 softmax scale, sign folding) and calls the launchers.
 // Nothing here allocates, frees or synchronises.
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -32,7 +33,9 @@ int check_ptrs(std::initializer_list<const void*> ps) {
 }
 
 void fill_scale(float scale, float& c2, uint32_t& qsign, float& qsign_f) {
-    c2 = fabsf(scale) * fa::kLog2e;
+    // c2 is kept at least FLT_MIN so that masked scores (-inf) times c2 stay
+    // -inf; for |scale| that small every exponent rounds to exp2(0) anyway.
+    c2 = fmaxf(fabsf(scale) * fa::kLog2e, FLT_MIN);
     const bool neg = signbit(scale) && scale != 0.0f;
     qsign = neg ? 0x80008000u : 0u;
     qsign_f = neg ? -1.0f : 1.0f;

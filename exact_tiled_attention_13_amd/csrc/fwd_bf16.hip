@@ -129,18 +129,21 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
     auto kbuf = [&](int i) { return smem + i * TILE; };
     auto vbuf = [&](int i) { return smem + (2 + i) * TILE; };
 
-    // Per-lane byte offsets of the MFMA operand reads.
-    int koff[DC];
-#pragma unroll
-    for (int cc = 0; cc < DC; ++cc) koff[cc] = l32 * RB + (((2 * cc + hi) ^ swk(l32)) << 4);
-    int voff[DB];
+    // Per-lane byte offsets of the MFMA operand reads. The swizzle only flips
+    // address bits that the row base leaves clear, so the offset of d chunk cc
+    // (K) or d block db (V) is the lane's base XOR a constant.
+    int kbase;
+    {
+        const int sw = swk(l32);
+        kbase = l32 * RB + ((hi ^ (sw & 1)) << 4) + ((sw >> 1) << 5);   // chunk pair cc: ^ (cc << 5)
+    }
+    int vbase;
     {
         const int g = lane >> 4, i = lane & 15;
         const int e = i >> 2;                              // key within the group of 4
         const int x = 2 * (g & 1) + ((i & 3) >> 1);        // chunk within the 64-byte run
         const int sq = (D == 128 ? e : (e >> 1));          // swizzle of that key row, in quads
-#pragma unroll
-        for (int db = 0; db < DB; ++db) voff[db] = (4 * hi + e) * RB + ((4 * (db ^ sq) + x) << 4) + ((i & 1) << 3);
+        vbase = (4 * hi + e) * RB + (sq << 6) + (x << 4) + ((i & 1) << 3);   // d block db: ^ (db << 6)
     }
 
     auto wave_active = [&](int t) { return !CAUSAL || (t * BN <= qw + 31); };
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
             s[kb] = f32x16{};
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * RB + koff[cc]);
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * RB + (kbase ^ (cc << 5)));
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cc], s[kb], 0, 0, 0);
             }
         }
@@ -167,29 +170,25 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
     // softmax of tile t held in s, then O^T += V_t^T P_t^T.
     auto softmax_pv = [&](int t, f32x16 (&s)[KB]) {
         const int j0 = t * BN;
+        // Tiles straddling the causal diagonal or the ragged end: masked
+        // scores become -inf (c2 > 0, so their exponentials are exactly 0).
         const bool masked = (CAUSAL && j0 + BN - 1 > qw) || (j0 + BN > N);
-        float mx = -INFINITY;
-        uint32_t dead[KB];  // bit u set: element u of block kb is masked
         if (masked) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                dead[kb] = 0u;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int key = j0 + kb * 32 + 8 * (u >> 2) + 4 * hi + (u & 3);
-                    const bool kill = key >= N || (CAUSAL && key > myq);
-                    dead[kb] |= (kill ? 1u : 0u) << u;
-                    if (!kill) mx = __builtin_fmaxf(mx, s[kb][u]);
-                }
-            }
-        } else {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int u = 0; u < 16; ++u) mx = __builtin_fmaxf(mx, s[kb][u]);
+                for (int u = 0; u < 16; ++u) {
+                    const int key = j0 + kb * 32 + 8 * (u >> 2) + 4 * hi + (u & 3);
+                    if (key >= N || (CAUSAL && key > myq)) s[kb][u] = -INFINITY;
+                }
         }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int u = 0; u < 16; ++u) mx = __builtin_fmaxf(mx, s[kb][u]);
         mx = max_halves(mx);
-        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+        const float mt = mx * c2;   // -inf when every key of the row is masked in this tile
         if (__builtin_amdgcn_ballot_w64(mt > m + kTau) != 0) {
             const float mnew = __builtin_fmaxf(m, mt);
             const float alpha = exp2_fast(m - mnew);
@@ -208,7 +207,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 p[u] = exp2_fast(__builtin_fmaf(s[kb][u], c2, -m));
-                if (masked) p[u] = ((dead[kb] >> u) & 1u) ? 0.f : p[u];
                 rowsum += p[u];
             }
 #pragma unroll
@@ -225,12 +223,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
         const unsigned char* Vs = vbuf(t & 1);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
+            const int voff = vbase ^ (db << 6);
 #pragma unroll
             for (int kc = 0; kc < BN / 16; ++kc) {
                 const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16_t*)(Vs + kc * 16 * RB + voff[db]));
+                    (lds_v4i16_t*)(Vs + kc * 16 * RB + voff));
                 const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16_t*)(Vs + (kc * 16 + 8) * RB + voff[db]));
+                    (lds_v4i16_t*)(Vs + (kc * 16 + 8) * RB + voff));
                 const v8i16 vv = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[kc],
                                                                    oacc[db], 0, 0, 0);
