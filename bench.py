@@ -93,7 +93,7 @@ def main():
     bufs = {}
     for c in masks:
         bufs[c] = dict(o=torch.empty_like(qd), lse=torch.empty((B, H, N), dtype=torch.float32, device=dev),
-                       dd=torch.empty((B, H, N), dtype=torch.float32, device=dev), dq=torch.empty_like(qd),
+                       ws=fa.workspace(B, H, N, d, dev), dq=torch.empty_like(qd),
                        dk=torch.empty_like(kd), dv=torch.empty_like(vd))
     scale = w.scale
     stream = torch.cuda.current_stream(dev)
@@ -107,9 +107,9 @@ def main():
         b = bufs[c]
         return [
             lambda: fa.attn_fwd(qd, kd, vd, c, scale, o=b["o"], lse=b["lse"]),
-            lambda: fa.attn_bwd_prep(b["o"], dod, dd=b["dd"]),
-            lambda: fa.attn_bwd_dkdv(qd, kd, vd, dod, b["lse"], b["dd"], c, scale, dk=b["dk"], dv=b["dv"]),
-            lambda: fa.attn_bwd_dq(qd, kd, vd, dod, b["lse"], b["dd"], c, scale, dq=b["dq"]),
+            lambda: fa.attn_bwd_prep(b["o"], dod, b["lse"], ws=b["ws"]),
+            lambda: fa.attn_bwd_dkdv(qd, kd, vd, dod, b["ws"], c, scale, dk=b["dk"], dv=b["dv"]),
+            lambda: fa.attn_bwd_dq(qd, kd, vd, dod, b["ws"], c, scale, dq=b["dq"]),
         ]
 
     calls = [f for c in masks for f in launches(c)]
@@ -147,7 +147,7 @@ def main():
         work[f"fwd_{tag}"] = ("mfma", 2 * f1)
         work[f"bwd_dkdv_{tag}"] = ("mfma", 4 * f1)     # S (recompute), dP, dV, dK
         work[f"bwd_dq_{tag}"] = ("mfma", 1 * f1)       # dQ (S, dP recomputed again: not counted)
-        work[f"bwd_prep_{tag}"] = ("hbm", 2.0 * B * N * H * d * 2 + 4.0 * B * H * N)
+        work[f"bwd_prep_{tag}"] = ("hbm", 2.0 * B * N * H * d * 2 + 4.0 * B * H * N + 8.0 * B * H * N)
     step_flops = sum(counted_fwd(B, H, N, d, c) * 3.5 for c in masks)
 
     breakdown = {}

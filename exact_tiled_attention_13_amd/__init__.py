@@ -25,4 +25,5 @@ from ._binding import (  # noqa: F401
     default_scale,
     lib,
     status_string,
+    workspace,
 )

@@ -57,11 +57,11 @@ def lib() -> ctypes.CDLL:
             L.attn_bwd_workspace_size.restype = sz
             L.attn_bwd.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, cf, vp]
             L.attn_bwd.restype = ci
-            L.attn_bwd_prep.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp]
+            L.attn_bwd_prep.argtypes = [vp, vp, vp, vp, sz, ci, ci, ci, ci, vp]
             L.attn_bwd_prep.restype = ci
-            L.attn_bwd_dkdv.argtypes = [vp] * 8 + [ci, ci, ci, ci, ci, cf, vp]
+            L.attn_bwd_dkdv.argtypes = [vp] * 5 + [sz, vp, vp, ci, ci, ci, ci, ci, cf, vp]
             L.attn_bwd_dkdv.restype = ci
-            L.attn_bwd_dq.argtypes = [vp] * 7 + [ci, ci, ci, ci, ci, cf, vp]
+            L.attn_bwd_dq.argtypes = [vp] * 5 + [sz, vp, ci, ci, ci, ci, ci, cf, vp]
             L.attn_bwd_dq.restype = ci
             L.fa_status_string.argtypes = [ci]
             L.fa_status_string.restype = ctypes.c_char_p
@@ -169,45 +169,51 @@ def attn_bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     return dq, dk, dv
 
 
-def attn_bwd_prep(o, do, dd=None):
-    """dd[b, h, i] = dO_i . O_i (fp32 [B, H, N]). Returns dd."""
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def workspace(B: int, H: int, N: int, d: int, device) -> torch.Tensor:
+    """A workspace tensor of attn_bwd_workspace_size bytes (uint8) on `device`."""
+    return torch.empty(attn_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=device)
+
+
+def attn_bwd_prep(o, do, lse, ws=None):
+    """Fill the backward workspace (D_i and LSE_i * log2 e). Returns the workspace."""
     B, N, H, d = _shape(o)
     dev = o.device
     _expect("o", o, (B, N, H, d), torch.bfloat16, dev)
     _expect("do", do, (B, N, H, d), torch.bfloat16, dev)
-    dd = torch.empty((B, H, N), dtype=torch.float32, device=dev) if dd is None else dd
-    _expect("dd", dd, (B, H, N), torch.float32, dev)
-    _check("attn_bwd_prep", lib().attn_bwd_prep(_ptr(o), _ptr(do), _ptr(dd), B, H, N, d, _stream(dev)))
-    return dd
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    ws = workspace(B, H, N, d, dev) if ws is None else ws
+    _check("attn_bwd_prep", lib().attn_bwd_prep(_ptr(o), _ptr(do), _ptr(lse), _ptr(ws), _nbytes(ws),
+                                                B, H, N, d, _stream(dev)))
+    return ws
 
 
-def attn_bwd_dkdv(q, k, v, do, lse, dd, causal: bool = False, scale: float | None = None, dk=None, dv=None):
-    """dK and dV from the forward inputs, dO, the forward's LSE and dd. Returns (dk, dv)."""
+def attn_bwd_dkdv(q, k, v, do, ws, causal: bool = False, scale: float | None = None, dk=None, dv=None):
+    """dK and dV from the forward inputs, dO and a workspace filled by attn_bwd_prep. Returns (dk, dv)."""
     B, N, H, d = _shape(q)
     dev = q.device
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dk", dk), ("dv", dv)):
         _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
-    _expect("lse", lse, (B, H, N), torch.float32, dev)
-    _expect("dd", dd, (B, H, N), torch.float32, dev)
     s = default_scale(d) if scale is None else float(scale)
-    _check("attn_bwd_dkdv", lib().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dd),
+    _check("attn_bwd_dkdv", lib().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(ws), _nbytes(ws),
                                                 _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), s,
                                                 _stream(dev)))
     return dk, dv
 
 
-def attn_bwd_dq(q, k, v, do, lse, dd, causal: bool = False, scale: float | None = None, dq=None):
-    """dQ from the forward inputs, dO, the forward's LSE and dd. Returns dq."""
+def attn_bwd_dq(q, k, v, do, ws, causal: bool = False, scale: float | None = None, dq=None):
+    """dQ from the forward inputs, dO and a workspace filled by attn_bwd_prep. Returns dq."""
     B, N, H, d = _shape(q)
     dev = q.device
     dq = torch.empty_like(q) if dq is None else dq
     for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dq", dq)):
         _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
-    _expect("lse", lse, (B, H, N), torch.float32, dev)
-    _expect("dd", dd, (B, H, N), torch.float32, dev)
     s = default_scale(d) if scale is None else float(scale)
-    _check("attn_bwd_dq", lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dd), _ptr(dq),
+    _check("attn_bwd_dq", lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(ws), _nbytes(ws), _ptr(dq),
                                             B, H, N, d, int(bool(causal)), s, _stream(dev)))
     return dq

@@ -41,9 +41,17 @@ void fill_scale(float scale, float& c2, uint32_t& qsign, float& qsign_f) {
     qsign_f = neg ? -1.0f : 1.0f;
 }
 
-size_t dd_bytes(int B, int H, int N) {
-    const size_t raw = (size_t)B * H * N * sizeof(float);
+// Backward workspace: D and LSE*log2(e), each fp32 [B, H, Npad], Npad = 64 * ceil(N / 64).
+size_t ws_half_elems(int B, int H, int N) { return (size_t)B * H * (size_t)((N + 63) & ~63); }
+
+size_t ws_bytes(int B, int H, int N) {
+    const size_t raw = 2 * ws_half_elems(B, H, N) * sizeof(float);
     return (raw + 255) & ~(size_t)255;
+}
+
+int check_ws(const void* ws, size_t bytes, int B, int H, int N) {
+    if (ws == nullptr || !aligned16(ws) || bytes < ws_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+    return FA_OK;
 }
 
 }  // namespace
@@ -79,30 +87,38 @@ int attn_fwd_fp32(const float* q, const float* k, const float* v, float* o, floa
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, int causal) {
     (void)causal;
     if (check_shape(B, H, N, d, 1.0f) != FA_OK) return 0;
-    return dd_bytes(B, H, N);
+    return ws_bytes(B, H, N);
 }
 
-int attn_bwd_prep(const void* o, const void* dO, float* dd, int B, int H, int N, int d, hipStream_t stream) {
+int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace, size_t workspace_bytes, int B,
+                  int H, int N, int d, hipStream_t stream) {
     int st = check_shape(B, H, N, d, 1.0f);
     if (st != FA_OK) return st;
-    st = check_ptrs({o, dO, dd});
+    st = check_ptrs({o, dO, lse});
+    if (st != FA_OK) return st;
+    st = check_ws(workspace, workspace_bytes, B, H, N);
     if (st != FA_OK) return st;
     fa::BwdArgs a{};
-    a.o = o; a.dO = dO; a.dd = dd;
+    a.o = o; a.dO = dO; a.lse = lse;
+    a.dd = static_cast<float*>(workspace);
+    a.lse2 = a.dd + ws_half_elems(B, H, N);
     a.B = B; a.H = H; a.N = N;
     return fa::launch_bwd_prep(a, d, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 namespace {
 
-int fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* dO, const float* lse,
-             const float* dd, int B, int H, int N, int d, float scale) {
+int fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+             size_t workspace_bytes, int B, int H, int N, int d, float scale) {
     int st = check_shape(B, H, N, d, scale);
     if (st != FA_OK) return st;
-    st = check_ptrs({q, k, v, dO, lse, dd});
+    st = check_ptrs({q, k, v, dO});
     if (st != FA_OK) return st;
-    a.q = q; a.k = k; a.v = v; a.dO = dO; a.lse = lse;
-    a.dd = const_cast<float*>(dd);
+    st = check_ws(workspace, workspace_bytes, B, H, N);
+    if (st != FA_OK) return st;
+    a.q = q; a.k = k; a.v = v; a.dO = dO;
+    a.dd = static_cast<float*>(const_cast<void*>(workspace));
+    a.lse2 = a.dd + ws_half_elems(B, H, N);
     a.B = B; a.H = H; a.N = N;
     a.scale = scale;
     float unused;
@@ -112,10 +128,11 @@ int fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const 
 
 }  // namespace
 
-int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* dd,
-                  void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                  size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                  hipStream_t stream) {
     fa::BwdArgs a{};
-    int st = fill_bwd(a, q, k, v, dO, lse, dd, B, H, N, d, scale);
+    int st = fill_bwd(a, q, k, v, dO, workspace, workspace_bytes, B, H, N, d, scale);
     if (st != FA_OK) return st;
     st = check_ptrs({dk, dv});
     if (st != FA_OK) return st;
@@ -123,10 +140,11 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, c
     return fa::launch_bwd_dkdv(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* dd,
-                void* dq, int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal, float scale,
+                hipStream_t stream) {
     fa::BwdArgs a{};
-    int st = fill_bwd(a, q, k, v, dO, lse, dd, B, H, N, d, scale);
+    int st = fill_bwd(a, q, k, v, dO, workspace, workspace_bytes, B, H, N, d, scale);
     if (st != FA_OK) return st;
     st = check_ptrs({dq});
     if (st != FA_OK) return st;
@@ -141,14 +159,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (st != FA_OK) return st;
     st = check_ptrs({q, k, v, o, dO, lse, dq, dk, dv});
     if (st != FA_OK) return st;
-    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < dd_bytes(B, H, N))
-        return FA_ERR_WORKSPACE;
-    float* dd = static_cast<float*>(workspace);
-    st = attn_bwd_prep(o, dO, dd, B, H, N, d, stream);
+    st = check_ws(workspace, workspace_bytes, B, H, N);
     if (st != FA_OK) return st;
-    st = attn_bwd_dkdv(q, k, v, dO, lse, dd, dk, dv, B, H, N, d, causal, scale, stream);
+    st = attn_bwd_prep(o, dO, lse, workspace, workspace_bytes, B, H, N, d, stream);
     if (st != FA_OK) return st;
-    return attn_bwd_dq(q, k, v, dO, lse, dd, dq, B, H, N, d, causal, scale, stream);
+    st = attn_bwd_dkdv(q, k, v, dO, workspace, workspace_bytes, dk, dv, B, H, N, d, causal, scale, stream);
+    if (st != FA_OK) return st;
+    return attn_bwd_dq(q, k, v, dO, workspace, workspace_bytes, dq, B, H, N, d, causal, scale, stream);
 }
 
 const char* fa_status_string(int status) {

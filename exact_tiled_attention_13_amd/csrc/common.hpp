@@ -51,7 +51,8 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* dd;        // workspace: D_i = dO_i . O_i, fp32 [B, H, N]
+    float* dd;        // workspace: D_i = dO_i . O_i, fp32 [B, H, Npad]
+    float* lse2;      // workspace: LSE_i * log2(e), fp32 [B, H, Npad] (+inf on padded rows)
     int B, H, N;
     float scale;      // the caller's scale (multiplies dQ and dK)
     float c2;         // |scale| * log2(e)

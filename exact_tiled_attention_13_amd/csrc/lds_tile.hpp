@@ -1,0 +1,83 @@
+// lds_tile.hpp -- LDS staging of 64-row bf16 tiles for the backward kernels.
+//
+// A tile is 64 rows of one head's [*, d] slice (row stride H*d elements in
+// global memory), stored in LDS unpadded, RB = 2d bytes per row, with the
+// 16-byte chunks of each row permuted by an XOR swizzle f(row). The swizzle is
+// chosen so that both access patterns the MFMA operands need are free of LDS
+// bank conflicts:
+//   * row reads (ds_read_b128): 16 consecutive rows at one chunk column;
+//   * transposing reads (ds_read_b64_tr_b16): 4 consecutive rows x 64 bytes.
+// Tiles are filled with direct-to-LDS loads (global_load_lds_dwordx4): one
+// wave instruction writes 1 KB of LDS, lane i its 16-byte slot i, so each lane
+// fetches the global chunk that the swizzle places in its slot.
+#pragma once
+
+#include "common.hpp"
+
+namespace fa {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+template <int D>
+struct LdsTile {
+    static constexpr int ROWS = 64;
+    static constexpr int RB = D * 2;            // bytes per row
+    static constexpr int BYTES = ROWS * RB;     // bytes per tile
+    static constexpr int NINST = BYTES / 1024;  // direct-to-LDS wave loads per tile
+    static constexpr int RPI = 1024 / RB;       // rows per such load
+    static constexpr int CPR = RB / 16;         // 16-byte chunks per row
+
+    // Chunk permutation of row r (4 bits for d = 128, 3 bits for d = 64).
+    __device__ static __forceinline__ int swz(int r) {
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
+
+    // Wave `w` of `nw` loads its share of rows row0 .. row0+63 of g (row
+    // stride rs elements) into the tile at `dst`. Rows at or past n are
+    // clamped to n - 1: callers mask them.
+    __device__ static __forceinline__ void load(unsigned char* dst, const __bf16* g, size_t rs, int row0, int n,
+                                                int w, int nw, int lane) {
+        for (int inst = w; inst < NINST; inst += nw) {
+            const int row = inst * RPI + lane / CPR;
+            const int c = (lane % CPR) ^ swz(row);
+            const int grow = min(row0 + row, n - 1);
+            __builtin_amdgcn_global_load_lds(g + (size_t)grow * rs + c * 8, (lds_void_t*)(dst + inst * 1024), 16,
+                                             0, 0);
+        }
+    }
+
+    // Row reads: A/B operand of a 32x32x16 MFMA whose 32 rows are tile rows
+    // rb*32 + lane%32 and whose K step cc covers d = cc*16 + (lane/32)*8 .. +8.
+    // Byte offset = rowbase(lane) ^ (cc << 5), plus rb*32*RB.
+    __device__ static __forceinline__ int rowbase(int lane) {
+        const int l32 = lane & 31, hi = lane >> 5;
+        const int f = swz(l32);
+        return l32 * RB + ((hi ^ (f & 1)) << 4) + ((f >> 1) << 5);
+    }
+
+    // Transposing reads: the 32x16 operand whose rows are d = db*32 + lane%32
+    // and whose K index runs over tile rows kc*16 + {4h..4h+3, 8+4h..8+4h+3}
+    // (h = lane/32), as two ds_read_b64_tr_b16 (half 0: first four rows,
+    // half 1: rows +8). Byte offset = trbase(lane, half) ^ (db << 6), plus
+    // kc*16*RB.
+    __device__ static __forceinline__ int trbase(int lane, int half) {
+        const int g = lane >> 4, i = lane & 15, hi = lane >> 5;
+        const int row = 4 * hi + (i >> 2) + 8 * half;            // row within the 16-row chunk
+        const int f = swz(row);
+        const int x = 2 * (g & 1) + ((i & 3) >> 1);               // 16-byte chunk within the 64-byte run
+        return row * RB + ((f >> 2) << 6) + ((x ^ (f & 3)) << 4) + ((i & 1) << 3);
+    }
+
+    __device__ static __forceinline__ bf16x8 read_row(const unsigned char* t, int off) {
+        return *reinterpret_cast<const bf16x8*>(t + off);
+    }
+
+    __device__ static __forceinline__ bf16x8 read_tr(const unsigned char* t, int off0, int off1) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(t + off0));
+        const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(t + off1));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+};
+
+}  // namespace fa

@@ -94,8 +94,9 @@ int attn_fwd_fp32(const float* q, const float* k, const float* v, float* o, floa
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for this
- * shape (the per-row statistic D_i = dO_i . O_i, fp32 [B, H, N], rounded up to
- * 256 bytes). Returns 0 for arguments attn_bwd would reject.
+ * shape: two fp32 arrays [B, H, Npad] with Npad = 64 * ceil(N / 64), the row
+ * statistics D_i = dO_i . O_i and LSE_i * log2(e), rounded up to 256 bytes.
+ * Returns 0 for arguments attn_bwd would reject.
  */
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, int causal);
 
@@ -123,22 +124,25 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 /*
  * The three stages attn_bwd runs, in order, on one stream. They are exported
  * so that a caller can time or schedule them separately; attn_bwd is exactly
- * attn_bwd_prep, then attn_bwd_dkdv, then attn_bwd_dq with dd = workspace.
+ * attn_bwd_prep, then attn_bwd_dkdv, then attn_bwd_dq on the same workspace.
  *
- * attn_bwd_prep -- dd[b, h, i] = sum_c dO[b, i, h, c] * O[b, i, h, c] in fp32
- *   (the row statistic D_i = sum_j P_ij dP_ij of the softmax backward).
- *   o, dO: [B, N, H, d] bf16 inputs; dd: fp32 [B, H, N] output.
- * attn_bwd_dkdv -- dk = scale * dS^T Q and dv = P^T dO, one workgroup per
- *   block of 128 keys looping over query tiles; reads dd from attn_bwd_prep.
- * attn_bwd_dq -- dq = scale * dS K, one workgroup per block of 128 queries
- *   looping over key tiles (recomputes P and dP); reads dd.
- * Arguments and errors as for attn_bwd; dd must be 16-byte aligned.
+ * attn_bwd_prep -- fills the workspace: D_i = sum_c dO[b, i, h, c] * O[b, i, h, c]
+ *   (the row statistic sum_j P_ij dP_ij of the softmax backward) and
+ *   LSE_i * log2(e), fp32, with D = 0 and LSE = +inf on the padded rows.
+ * attn_bwd_dkdv -- dk = scale * dS^T Q and dv = P^T dO: one workgroup per
+ *   block of 128 keys, looping over query tiles; reads the workspace.
+ * attn_bwd_dq -- dq = scale * dS K: one workgroup per block of 256 queries,
+ *   looping over key tiles (recomputes P and dP); reads the workspace.
+ * Arguments and errors as for attn_bwd.
  */
-int attn_bwd_prep(const void* o, const void* dO, float* dd, int B, int H, int N, int d, hipStream_t stream);
-int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* dd,
-                  void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
-int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* dd,
-                void* dq, int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace, size_t workspace_bytes,
+                  int B, int H, int N, int d, hipStream_t stream);
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                  size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                  hipStream_t stream);
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal, float scale,
+                hipStream_t stream);
 
 /* fa_status_string -- static, human-readable name of a status code. Never NULL. */
 const char* fa_status_string(int status);

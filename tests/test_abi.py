@@ -85,8 +85,30 @@ def test_backward_rejects_bad_arguments():
 
 
 def test_workspace_size():
-    assert fa.attn_bwd_workspace_size(1, 1, 16, 64, False) == 256
-    assert fa.attn_bwd_workspace_size(4, 16, 4096, 128, True) == 4 * 16 * 4096 * 4
-    assert fa.attn_bwd_workspace_size(1, 1, 65, 64, False) == 512  # 260 bytes rounded up to 256
+    # two fp32 arrays [B, H, 64 * ceil(N / 64)], rounded up to 256 bytes
+    assert fa.attn_bwd_workspace_size(1, 1, 16, 64, False) == 512
+    assert fa.attn_bwd_workspace_size(4, 16, 4096, 128, True) == 2 * 4 * 16 * 4096 * 4
+    assert fa.attn_bwd_workspace_size(1, 1, 65, 64, False) == 1024
+    assert fa.attn_bwd_workspace_size(3, 1, 1, 64, False) == 1536  # 2 * 3 * 64 * 4, already a multiple of 256
     assert fa.attn_bwd_workspace_size(0, 1, 16, 64, False) == 0
     assert fa.attn_bwd_workspace_size(1, 1, 16, 96, False) == 0
+
+
+def test_backward_stages_reject_bad_arguments():
+    L = fa.lib()
+    need = fa.attn_bwd_workspace_size(1, 1, 16, 64, False)
+    # attn_bwd_prep(o, dO, lse, ws, ws_bytes, B, H, N, d, stream)
+    assert L.attn_bwd_prep(0, P, P, P, need, 1, 1, 16, 64, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_prep(P, P, 0, P, need, 1, 1, 16, 64, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_prep(P, P, P, P, need - 1, 1, 1, 16, 64, None) == fa.FA_ERR_WORKSPACE
+    assert L.attn_bwd_prep(P, P, P, 0, need, 1, 1, 16, 64, None) == fa.FA_ERR_WORKSPACE
+    assert L.attn_bwd_prep(P, P, P, P, need, 1, 1, 16, 48, None) == fa.FA_ERR_UNSUPPORTED
+    # attn_bwd_dkdv(q, k, v, dO, ws, ws_bytes, dk, dv, B, H, N, d, causal, scale, stream)
+    assert L.attn_bwd_dkdv(P, P, P, P, P, need, 0, P, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_dkdv(P, P, P, P, P, need - 1, P, P, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_WORKSPACE
+    assert L.attn_bwd_dkdv(P, P, MIS, P, P, need, P, P, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_dkdv(P, P, P, P, P, need, P, P, 1, 1, 16, 64, 0, float("nan"), None) == fa.FA_ERR_INVALID_ARG
+    # attn_bwd_dq(q, k, v, dO, ws, ws_bytes, dq, B, H, N, d, causal, scale, stream)
+    assert L.attn_bwd_dq(P, P, P, P, P, need, 0, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_dq(P, P, P, P, 0, need, P, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_WORKSPACE
+    assert L.attn_bwd_dq(P, P, P, P, P, need, P, 1, 0, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
