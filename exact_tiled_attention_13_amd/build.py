@@ -34,9 +34,16 @@ FLAGS = [
 ]
 
 
+# The backward dK/dV kernel runs one wave per SIMD with more live state than
+# 256 VGPRs; by default every MFMA of such a kernel writes AGPRs, and the
+# softmax then copies S and dP back to VGPRs each tile. The VGPR form keeps
+# S / dP in VGPRs (the accumulators that do not fit spill to AGPRs instead).
+EXTRA_FLAGS = {"bwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -24,8 +24,6 @@
 // Workspace: two fp32 arrays [B, H, Npad] (Npad = 64 * ceil(N / 64)), first
 // D_i, then LSE_i * log2(e); padded rows hold D = 0 and LSE = +inf, so their
 // probabilities are exactly 0.
-#include <type_traits>
-
 #include "common.hpp"
 #include "kernels.hpp"
 #include "lds_tile.hpp"
@@ -146,8 +144,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     auto dma = [&](int t, int s) {
         unsigned char* st = stage_ptr(s);
         const int q0 = qstart + t * BQ;
-        T::load(st, Qg, rs, q0, N, wave, NW, lane);
-        T::load(st + T::BYTES, dOg, rs, q0, N, wave, NW, lane);
+        T::template load<NW>(st, Qg, rs, q0, N, wave, lane);
+        T::template load<NW>(st + T::BYTES, dOg, rs, q0, N, wave, lane);
         // q0 + 63 < npad: the padded statistics need no clamp.
         if (wave == 0)
             __builtin_amdgcn_global_load_lds(lsg + q0 + lane, (lds_void_t*)(st + 2 * T::BYTES), 4, 0, 0);
@@ -156,14 +154,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
-    auto tile = [&](int t, auto masked_c) {
-        constexpr bool MASKED = decltype(masked_c)::value;
+    auto tile = [&](int t, bool masked) {
         const int q0 = qstart + t * BQ;
         const unsigned char* Qs = stage_ptr(t & 1);
         const unsigned char* Gs = Qs + T::BYTES;
         const float* Ls = reinterpret_cast<const float*>(Qs + 2 * T::BYTES);
         const float* Ds = Ls + BQ;
-        bf16x8 pb[BQ / 16], sb[BQ / 16];
+        // One 32-query block at a time: S, dP, then P and dS, then its two
+        // 16-query chunks of dV^T += dO^T P and dK^T += Q^T dS.
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x16 s = f32x16{}, dp = f32x16{};
@@ -173,13 +171,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Qs, off), kf[cc], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Gs, off), vf[cc], dp, 0, 0, 0);
             }
-            if constexpr (MASKED) {
+            if (masked) {
                 // Causal diagonal: key myk is invisible to queries before it.
+                // Query of element u is q0 + mb*32 + 4*hi + 8*(u/4) + u%4.
+                const int thr = myk - (q0 + mb * 32 + 4 * hi);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int q = q0 + mb * 32 + 8 * (u >> 2) + 4 * hi + (u & 3);
-                    if (myk > q) s[u] = -INFINITY;
-                }
+                for (int u = 0; u < 16; ++u)
+                    if (thr > 8 * (u >> 2) + (u & 3)) s[u] = -INFINITY;
             }
             float p[16], ds[16];
 #pragma unroll
@@ -194,6 +192,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                     ds[u] = p[u] * (dp[u] - d4[e]);
                 }
             }
+            bf16x8 pb[2], sb[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 u32x4 wp, wd;
@@ -202,19 +201,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                     wp[e] = pack_bf16x2(p[half * 8 + 2 * e], p[half * 8 + 2 * e + 1]);
                     wd[e] = pack_bf16x2(ds[half * 8 + 2 * e], ds[half * 8 + 2 * e + 1]);
                 }
-                pb[mb * 2 + half] = as_bf16x8(wp);
-                sb[mb * 2 + half] = as_bf16x8(wd);
+                pb[half] = as_bf16x8(wp);
+                sb[half] = as_bf16x8(wd);
             }
-        }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int o0 = trb0 ^ (db << 6), o1 = trb1 ^ (db << 6);
+            for (int db = 0; db < DB; ++db) {
+                const int o0 = trb0 ^ (db << 6), o1 = trb1 ^ (db << 6);
 #pragma unroll
-            for (int qc = 0; qc < BQ / 16; ++qc) {
-                const bf16x8 ga = T::read_tr(Gs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
-                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb[qc], dvacc[db], 0, 0, 0);
-                const bf16x8 qa = T::read_tr(Qs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
-                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[qc], dkacc[db], 0, 0, 0);
+                for (int half = 0; half < 2; ++half) {
+                    const int qc = mb * 2 + half;
+                    const bf16x8 ga = T::read_tr(Gs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
+                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb[half], dvacc[db], 0, 0, 0);
+                    const bf16x8 qa = T::read_tr(Qs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
+                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[half], dkacc[db], 0, 0, 0);
+                }
             }
         }
     };
@@ -226,12 +226,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
         const int q0 = qstart + t * BQ;
         // Causal: tiles whose last query precedes this wave's first key are empty.
-        if (!CAUSAL || q0 + BQ - 1 >= kw) {
-            if (CAUSAL && q0 < kw + 31)
-                tile(t, std::true_type{});
-            else
-                tile(t, std::false_type{});
-        }
+        if (!CAUSAL || q0 + BQ - 1 >= kw) tile(t, CAUSAL && q0 < kw + 31);
         wait_dma();
         __syncthreads();
     }
@@ -330,13 +325,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     auto kbuf = [&](int s) { return smem + s * T::BYTES; };
     auto vbuf = [&](int s) { return smem + (2 + s) * T::BYTES; };
     auto dma = [&](int t, int s) {
-        T::load(kbuf(s), Kg, rs, t * BN, N, wave, NW, lane);
-        T::load(vbuf(s), Vg, rs, t * BN, N, wave, NW, lane);
+        T::template load<NW>(kbuf(s), Kg, rs, t * BN, N, wave, lane);
+        T::template load<NW>(vbuf(s), Vg, rs, t * BN, N, wave, lane);
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
-    auto tile = [&](int t, auto masked_c) {
-        constexpr bool MASKED = decltype(masked_c)::value;
+    auto tile = [&](int t, bool masked) {
         const int j0 = t * BN;
         const unsigned char* Ks = kbuf(t & 1);
         const unsigned char* Vs = vbuf(t & 1);
@@ -350,12 +344,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Ks, off), qf[cc], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Vs, off), gf[cc], dp, 0, 0, 0);
             }
-            if constexpr (MASKED) {
+            if (masked) {
+                // Keys past the end, and under the causal mask keys after the
+                // query. Key of element u is j0 + kb*32 + 4*hi + 8*(u/4) + u%4.
+                const int k0u = j0 + kb * 32 + 4 * hi;
+                const int lim = CAUSAL ? min(N - 1, myq) : N - 1;   // last visible key
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int key = j0 + kb * 32 + 8 * (u >> 2) + 4 * hi + (u & 3);
-                    if (key >= N || (CAUSAL && key > myq)) s[u] = -INFINITY;
-                }
+                for (int u = 0; u < 16; ++u)
+                    if (k0u + 8 * (u >> 2) + (u & 3) > lim) s[u] = -INFINITY;
             }
             float ds[16];
 #pragma unroll
@@ -385,12 +381,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     for (int t = 0; t < ntiles; ++t) {
         if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
         const int j0 = t * BN;
-        if (!CAUSAL || j0 <= qw + 31) {
-            if ((CAUSAL && j0 + BN - 1 > qw) || (j0 + BN > N))
-                tile(t, std::true_type{});
-            else
-                tile(t, std::false_type{});
-        }
+        if (!CAUSAL || j0 <= qw + 31) tile(t, (CAUSAL && j0 + BN - 1 > qw) || (j0 + BN > N));
         wait_dma();
         __syncthreads();
     }

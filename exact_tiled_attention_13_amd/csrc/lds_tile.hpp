@@ -33,12 +33,16 @@ struct LdsTile {
         return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
     }
 
-    // Wave `w` of `nw` loads its share of rows row0 .. row0+63 of g (row
+    // Wave `w` of NW loads its share of rows row0 .. row0+63 of g (row
     // stride rs elements) into the tile at `dst`. Rows at or past n are
     // clamped to n - 1: callers mask them.
+    template <int NW>
     __device__ static __forceinline__ void load(unsigned char* dst, const __bf16* g, size_t rs, int row0, int n,
-                                                int w, int nw, int lane) {
-        for (int inst = w; inst < NINST; inst += nw) {
+                                                int w, int lane) {
+        static_assert(NINST % NW == 0, "tile loads must split evenly over the waves");
+#pragma unroll
+        for (int j = 0; j < NINST / NW; ++j) {
+            const int inst = w + NW * j;
             const int row = inst * RPI + lane / CPR;
             const int c = (lane % CPR) ^ swz(row);
             const int grow = min(row0 + row, n - 1);
