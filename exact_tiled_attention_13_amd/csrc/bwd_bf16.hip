@@ -164,13 +164,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         // 16-query chunks of dV^T += dO^T P and dK^T += Q^T dS.
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // Operand reads are issued ahead of the MFMAs that consume them:
+            // with one wave per SIMD nothing else hides the LDS latency.
+            bf16x8 qa[DC], ga[DC];
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc) {
                 const int off = (rowb ^ (cc << 5)) + mb * 32 * RB;
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Qs, off), kf[cc], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Gs, off), vf[cc], dp, 0, 0, 0);
+                qa[cc] = T::read_row(Qs, off);
+                ga[cc] = T::read_row(Gs, off);
             }
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[cc], kf[cc], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[cc], vf[cc], dp, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * DC, 0);   // all 16 row reads first
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * DC, 0);   // then the 16 MFMAs
             if (masked) {
                 // Causal diagonal: key myk is invisible to queries before it.
                 // Query of element u is q0 + mb*32 + 4*hi + 8*(u/4) + u%4.
@@ -204,18 +214,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                 pb[half] = as_bf16x8(wp);
                 sb[half] = as_bf16x8(wd);
             }
+            bf16x8 gt[DB][2], qt[DB][2];
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int o0 = trb0 ^ (db << 6), o1 = trb1 ^ (db << 6);
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int qc = mb * 2 + half;
-                    const bf16x8 ga = T::read_tr(Gs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
-                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb[half], dvacc[db], 0, 0, 0);
-                    const bf16x8 qa = T::read_tr(Qs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
-                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[half], dkacc[db], 0, 0, 0);
+                    gt[db][half] = T::read_tr(Gs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
+                    qt[db][half] = T::read_tr(Qs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
                 }
             }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt[db][half], pb[half], dvacc[db], 0, 0, 0);
+                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db][half], sb[half], dkacc[db], 0, 0, 0);
+                }
         }
     };
 
