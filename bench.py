@@ -32,6 +32,38 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 
 
+CSRC = os.path.join(ROOT, "exact_tiled_attention_13_amd", "csrc")
+TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash(name: str) -> str:
+    """sha256 over the sources and build script a kernel is compiled from; the
+    HBM byte counts stored in profiles/ are used only while this matches."""
+    import hashlib
+
+    main = "fwd_bf16.hip" if name.startswith("fwd") else "bwd_bf16.hip"
+    h = hashlib.sha256()
+    for f in [os.path.join(CSRC, x) for x in ("common.hpp", "lds_tile.hpp", "kernels.hpp", main)] + [
+            os.path.join(ROOT, "exact_tiled_attention_13_amd", "build.py")]:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch of kernel `name` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), or
+    None when no such measurement exists for the current kernel source."""
+    try:
+        with open(TRAFFIC) as f:
+            entry = json.load(f)["kernels"].get(name)
+    except (OSError, ValueError, KeyError):
+        return None
+    if not entry or entry.get("source_sha256") != kernel_source_hash(name):
+        return None
+    return float(entry["hbm_bytes"])
+
+
 def counted_fwd(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
@@ -176,10 +208,11 @@ def main():
     achieved = amount / (kern_ms[dom] * 1e-3)
     if kind == "mfma":
         roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom)}
     else:
         roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(achieved / 1e9 / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom)}
     roof["kernel"] = dom
     roof["work_per_launch"] = amount
     roof["avg_launch_ms"] = round(kern_ms[dom], 4)
