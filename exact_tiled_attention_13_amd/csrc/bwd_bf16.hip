@@ -154,84 +154,123 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
+    // The tile is two 32-query blocks. Per block: S = Q K^T and dP = dO V^T
+    // (16 MFMAs), then P and dS (VALU), then dV^T += dO^T P and dK^T += Q^T dS
+    // (16 MFMAs). With one wave per SIMD nothing hides latency but the wave's
+    // own instruction order, so the tile is scheduled by hand: operand reads
+    // run PF MFMAs ahead, and the softmax of one block is cut into slices
+    // placed between the MFMAs of the next phase:
+    //   S/dP(0); S/dP(1) + softmax(0); dV/dK(0) + softmax(1); dV/dK(1).
+    // sched_barrier(0) fences keep the compiler from regrouping the stream.
+    constexpr int PF = 3;                // prefetch distance, in MFMA pairs
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+    struct Soft {                        // softmax state of one 32-query block
+        f32x16 s, dp;
+        float p[16], ds[16];
+        bf16x8 pb[2], sb[2];
+    };
+    // Softmax slice k (0..5) of block mb: slices 0-3 handle element groups
+    // g4 = k (4 elements each), slices 4-5 pack half k-4 into bf16 operands.
+    auto soft_slice = [&](Soft& x, const float* Ls, const float* Ds, int mb, int thr, int k) {
+        if (k < 4) {
+            const int g4 = k;
+            const int ql = mb * 32 + 8 * g4 + 4 * hi;   // tile-local query of element 4*g4
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int u = 4 * g4 + e;
+                float sv = x.s[u];
+                // Causal diagonal: key myk is invisible to queries before it;
+                // thr is the key minus the element-0 query (very negative off
+                // the diagonal).
+                if (CAUSAL) sv = (thr > 8 * g4 + e) ? -INFINITY : sv;
+                x.p[u] = exp2_fast(__builtin_fmaf(sv, c2, -l4[e]));
+                x.ds[u] = x.p[u] * (x.dp[u] - d4[e]);
+            }
+        } else {
+            const int half = k - 4;
+            u32x4 wp, wd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                wp[e] = pack_bf16x2(x.p[half * 8 + 2 * e], x.p[half * 8 + 2 * e + 1]);
+                wd[e] = pack_bf16x2(x.ds[half * 8 + 2 * e], x.ds[half * 8 + 2 * e + 1]);
+            }
+            x.pb[half] = as_bf16x8(wp);
+            x.sb[half] = as_bf16x8(wd);
+        }
+    };
+
     auto tile = [&](int t, bool masked) {
+        static_assert(MB == 2, "the schedule below is written for two 32-query blocks");
         const int q0 = qstart + t * BQ;
         const unsigned char* Qs = stage_ptr(t & 1);
         const unsigned char* Gs = Qs + T::BYTES;
         const float* Ls = reinterpret_cast<const float*>(Qs + 2 * T::BYTES);
         const float* Ds = Ls + BQ;
-        // One 32-query block at a time: S, dP, then P and dS, then its two
-        // 16-query chunks of dV^T += dO^T P and dK^T += Q^T dS.
+        const int thr[2] = {masked ? myk - (q0 + 4 * hi) : -(1 << 30), masked ? myk - (q0 + 32 + 4 * hi) : -(1 << 30)};
+        Soft x[2];
+
+        // Phase S/dP: step i in 0..2*DC-1 covers block i/DC, d chunk i%DC.
+        bf16x8 ra[2 * DC], rb[2 * DC];
+        auto row_load = [&](int i) {
+            const int off = (rowb ^ ((i % DC) << 5)) + (i / DC) * 32 * RB;
+            ra[i] = T::read_row(Qs, off);
+            rb[i] = T::read_row(Gs, off);
+        };
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            // Operand reads are issued ahead of the MFMAs that consume them:
-            // with one wave per SIMD nothing else hides the LDS latency.
-            bf16x8 qa[DC], ga[DC];
+        for (int i = 0; i < PF; ++i) row_load(i);
+        fence();
 #pragma unroll
-            for (int cc = 0; cc < DC; ++cc) {
-                const int off = (rowb ^ (cc << 5)) + mb * 32 * RB;
-                qa[cc] = T::read_row(Qs, off);
-                ga[cc] = T::read_row(Gs, off);
+        for (int i = 0; i < 2 * DC; ++i) {
+            Soft& y = x[i / DC];
+            const int cc = i % DC;
+            if (cc == 0) {
+                y.s = f32x16{};
+                y.dp = f32x16{};
             }
-            f32x16 s = f32x16{}, dp = f32x16{};
+            y.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i], kf[cc], y.s, 0, 0, 0);
+            y.dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[i], vf[cc], y.dp, 0, 0, 0);
+            if (i + PF < 2 * DC) row_load(i + PF);
+            // Block 0's softmax runs under block 1's S/dP MFMAs.
+            // (six slices spread over the DC steps of block 1)
+            if (i >= DC) {
 #pragma unroll
-            for (int cc = 0; cc < DC; ++cc) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[cc], kf[cc], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[cc], vf[cc], dp, 0, 0, 0);
+                for (int k = 0; k < 6; ++k)
+                    if (k * DC / 6 == i - DC) soft_slice(x[0], Ls, Ds, 0, thr[0], k);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * DC, 0);   // all 16 row reads first
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * DC, 0);   // then the 16 MFMAs
-            if (masked) {
-                // Causal diagonal: key myk is invisible to queries before it.
-                // Query of element u is q0 + mb*32 + 4*hi + 8*(u/4) + u%4.
-                const int thr = myk - (q0 + mb * 32 + 4 * hi);
+            fence();
+        }
+
+        // Phase dV/dK: step j in 0..2*2*DB-1 covers block j/(2DB), d block
+        // (j/2)%DB, 16-query half j%2.
+        constexpr int NJ = 2 * 2 * DB;
+        bf16x8 ta[NJ], tb[NJ];
+        auto tr_load = [&](int j) {
+            const int mb = j / (2 * DB), db = (j / 2) % DB, half = j % 2;
+            const int qc = mb * 2 + half;
+            const int o0 = (trb0 ^ (db << 6)) + qc * 16 * RB, o1 = (trb1 ^ (db << 6)) + qc * 16 * RB;
+            ta[j] = T::read_tr(Gs, o0, o1);
+            tb[j] = T::read_tr(Qs, o0, o1);
+        };
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (thr > 8 * (u >> 2) + (u & 3)) s[u] = -INFINITY;
+        for (int j = 0; j < PF; ++j) tr_load(j);
+        fence();
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int mb = j / (2 * DB), db = (j / 2) % DB, half = j % 2;
+            dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j], x[mb].pb[half], dvacc[db], 0, 0, 0);
+            dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[j], x[mb].sb[half], dkacc[db], 0, 0, 0);
+            if (j + PF < NJ) tr_load(j + PF);
+            // Block 1's softmax runs under block 0's dV/dK MFMAs.
+            // (six slices spread over the 2*DB steps of block 0)
+            if (mb == 0) {
+#pragma unroll
+                for (int k = 0; k < 6; ++k)
+                    if (k * (2 * DB) / 6 == j) soft_slice(x[1], Ls, Ds, 1, thr[1], k);
             }
-            float p[16], ds[16];
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int ql = mb * 32 + 8 * g4 + 4 * hi;   // tile-local query of element 4*g4
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int u = 4 * g4 + e;
-                    p[u] = exp2_fast(__builtin_fmaf(s[u], c2, -l4[e]));
-                    ds[u] = p[u] * (dp[u] - d4[e]);
-                }
-            }
-            bf16x8 pb[2], sb[2];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                u32x4 wp, wd;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    wp[e] = pack_bf16x2(p[half * 8 + 2 * e], p[half * 8 + 2 * e + 1]);
-                    wd[e] = pack_bf16x2(ds[half * 8 + 2 * e], ds[half * 8 + 2 * e + 1]);
-                }
-                pb[half] = as_bf16x8(wp);
-                sb[half] = as_bf16x8(wd);
-            }
-            bf16x8 gt[DB][2], qt[DB][2];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int o0 = trb0 ^ (db << 6), o1 = trb1 ^ (db << 6);
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int qc = mb * 2 + half;
-                    gt[db][half] = T::read_tr(Gs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
-                    qt[db][half] = T::read_tr(Qs, o0 + qc * 16 * RB, o1 + qc * 16 * RB);
-                }
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt[db][half], pb[half], dvacc[db], 0, 0, 0);
-                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db][half], sb[half], dkacc[db], 0, 0, 0);
-                }
+            fence();
         }
     };
 
