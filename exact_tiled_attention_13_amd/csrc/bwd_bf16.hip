@@ -24,6 +24,8 @@
 // Workspace: two fp32 arrays [B, H, Npad] (Npad = 64 * ceil(N / 64)), first
 // D_i, then LSE_i * log2(e); padded rows hold D = 0 and LSE = +inf, so their
 // probabilities are exactly 0.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "lds_tile.hpp"
@@ -172,7 +174,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     };
     // Softmax slice k (0..5) of block mb: slices 0-3 handle element groups
     // g4 = k (4 elements each), slices 4-5 pack half k-4 into bf16 operands.
-    auto soft_slice = [&](Soft& x, const float* Ls, const float* Ds, int mb, int thr, int k) {
+    auto soft_slice = [&](Soft& x, const float* Ls, const float* Ds, int mb, int thr, int k, auto masked_c) {
+        constexpr bool MASKED = decltype(masked_c)::value;
         if (k < 4) {
             const int g4 = k;
             const int ql = mb * 32 + 8 * g4 + 4 * hi;   // tile-local query of element 4*g4
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                 // Causal diagonal: key myk is invisible to queries before it;
                 // thr is the key minus the element-0 query (very negative off
                 // the diagonal).
-                if (CAUSAL) sv = (thr > 8 * g4 + e) ? -INFINITY : sv;
+                if constexpr (MASKED) sv = (thr > 8 * g4 + e) ? -INFINITY : sv;
                 x.p[u] = exp2_fast(__builtin_fmaf(sv, c2, -l4[e]));
                 x.ds[u] = x.p[u] * (x.dp[u] - d4[e]);
             }
@@ -202,8 +205,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
     };
 
-    auto tile = [&](int t, bool masked) {
+    auto tile = [&](int t, auto masked_c) {
         static_assert(MB == 2, "the schedule below is written for two 32-query blocks");
+        constexpr bool masked = decltype(masked_c)::value;
         const int q0 = qstart + t * BQ;
         const unsigned char* Qs = stage_ptr(t & 1);
         const unsigned char* Gs = Qs + T::BYTES;
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             if (i >= DC) {
 #pragma unroll
                 for (int k = 0; k < 6; ++k)
-                    if (k * DC / 6 == i - DC) soft_slice(x[0], Ls, Ds, 0, thr[0], k);
+                    if (k * DC / 6 == i - DC) soft_slice(x[0], Ls, Ds, 0, thr[0], k, masked_c);
             }
             fence();
         }
@@ -268,20 +272,29 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             if (mb == 0) {
 #pragma unroll
                 for (int k = 0; k < 6; ++k)
-                    if (k * (2 * DB) / 6 == j) soft_slice(x[1], Ls, Ds, 1, thr[1], k);
+                    if (k * (2 * DB) / 6 == j) soft_slice(x[1], Ls, Ds, 1, thr[1], k, masked_c);
             }
             fence();
         }
     };
 
+    // Causal: only the first BK / BQ tiles (queries k0 .. k0+BK-1) straddle the
+    // diagonal of this workgroup's keys; they run the masked variant, the
+    // rest the variant without mask arithmetic.
+    const int t_split = CAUSAL ? min(ntiles, BK / BQ) : 0;
     dma(0, 0);
     wait_dma();
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = 0; t < t_split; ++t) {
         if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
-        const int q0 = qstart + t * BQ;
-        // Causal: tiles whose last query precedes this wave's first key are empty.
-        if (!CAUSAL || q0 + BQ - 1 >= kw) tile(t, CAUSAL && q0 < kw + 31);
+        // Tiles whose last query precedes this wave's first key are empty.
+        if (qstart + t * BQ + BQ - 1 >= kw) tile(t, std::true_type{});
+        wait_dma();
+        __syncthreads();
+    }
+    for (int t = t_split; t < ntiles; ++t) {
+        if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
+        tile(t, std::false_type{});
         wait_dma();
         __syncthreads();
     }
@@ -385,7 +398,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
-    auto tile = [&](int t, bool masked) {
+    auto tile = [&](int t, auto masked_c) {
+        constexpr bool MASKED = decltype(masked_c)::value;
         const int j0 = t * BN;
         const unsigned char* Ks = kbuf(t & 1);
         const unsigned char* Vs = vbuf(t & 1);
@@ -399,14 +413,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Ks, off), qf[cc], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Vs, off), gf[cc], dp, 0, 0, 0);
             }
-            if (masked) {
+            if constexpr (MASKED) {
                 // Keys past the end, and under the causal mask keys after the
                 // query. Key of element u is j0 + kb*32 + 4*hi + 8*(u/4) + u%4.
-                const int k0u = j0 + kb * 32 + 4 * hi;
-                const int lim = CAUSAL ? min(N - 1, myq) : N - 1;   // last visible key
+                const int thr = (CAUSAL ? min(N - 1, myq) : N - 1) - (j0 + kb * 32 + 4 * hi);
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (k0u + 8 * (u >> 2) + (u & 3) > lim) s[u] = -INFINITY;
+                for (int u = 0; u < 16; ++u) s[u] = (8 * (u >> 2) + (u & 3) > thr) ? -INFINITY : s[u];
             }
             float ds[16];
 #pragma unroll
@@ -430,13 +442,22 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
         }
     };
 
+    // Tiles before t_split need no mask for any wave of the workgroup (they
+    // end before the first query and before N); the rest run the masked
+    // variant. The split keeps mask arithmetic out of the main loop.
+    const int t_split = min(CAUSAL ? q0 / BN : ntiles, (N % BN) ? ntiles - 1 : ntiles);
     dma(0, 0);
     wait_dma();
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = 0; t < t_split; ++t) {
         if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
-        const int j0 = t * BN;
-        if (!CAUSAL || j0 <= qw + 31) tile(t, (CAUSAL && j0 + BN - 1 > qw) || (j0 + BN > N));
+        tile(t, std::false_type{});
+        wait_dma();
+        __syncthreads();
+    }
+    for (int t = t_split; t < ntiles; ++t) {
+        if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
+        if (!CAUSAL || t * BN <= qw + 31) tile(t, std::true_type{});
         wait_dma();
         __syncthreads();
     }
