@@ -398,6 +398,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
+    // Per tile: for each 32-key block, S^T and dP^T (16 MFMAs) then dS (VALU);
+    // then dQ^T += K^T dS^T (16 MFMAs). Operand reads are issued PF MFMAs
+    // ahead of their use and fenced so the compiler keeps that order.
+    constexpr int PF = 4;
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
     auto tile = [&](int t, auto masked_c) {
         constexpr bool MASKED = decltype(masked_c)::value;
         const int j0 = t * BN;
@@ -407,11 +412,21 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             f32x16 s = f32x16{}, dp = f32x16{};
+            bf16x8 ra[DC], rb[DC];
+            auto row_load = [&](int cc) {
+                const int off = (rowb ^ (cc << 5)) + kb * 32 * RB;
+                ra[cc] = T::read_row(Ks, off);
+                rb[cc] = T::read_row(Vs, off);
+            };
+#pragma unroll
+            for (int cc = 0; cc < PF; ++cc) row_load(cc);
+            fence();
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc) {
-                const int off = (rowb ^ (cc << 5)) + kb * 32 * RB;
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Ks, off), qf[cc], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::read_row(Vs, off), gf[cc], dp, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[cc], qf[cc], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[cc], gf[cc], dp, 0, 0, 0);
+                if (cc + PF < DC) row_load(cc + PF);
+                fence();
             }
             if constexpr (MASKED) {
                 // Keys past the end, and under the causal mask keys after the
@@ -430,15 +445,23 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
                 for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(ds[half * 8 + 2 * e], ds[half * 8 + 2 * e + 1]);
                 sb[kb * 2 + half] = as_bf16x8(w);
             }
+            fence();
         }
+        constexpr int NJ = DB * (BN / 16);
+        bf16x8 ka[NJ];
+        auto tr_load = [&](int j) {
+            const int db = j / (BN / 16), kc = j % (BN / 16);
+            ka[j] = T::read_tr(Ks, (trb0 ^ (db << 6)) + kc * 16 * RB, (trb1 ^ (db << 6)) + kc * 16 * RB);
+        };
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int o0 = trb0 ^ (db << 6), o1 = trb1 ^ (db << 6);
+        for (int j = 0; j < PF; ++j) tr_load(j);
+        fence();
 #pragma unroll
-            for (int kc = 0; kc < BN / 16; ++kc) {
-                const bf16x8 ka = T::read_tr(Ks, o0 + kc * 16 * RB, o1 + kc * 16 * RB);
-                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sb[kc], dqacc[db], 0, 0, 0);
-            }
+        for (int j = 0; j < NJ; ++j) {
+            const int db = j / (BN / 16), kc = j % (BN / 16);
+            dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], sb[kc], dqacc[db], 0, 0, 0);
+            if (j + PF < NJ) tr_load(j + PF);
+            fence();
         }
     };
 
