@@ -146,7 +146,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
         vbase = (4 * hi + e) * RB + (sq << 6) + (x << 4) + ((i & 1) << 3);   // d block db: ^ (db << 6)
     }
 
-    auto wave_active = [&](int t) { return !CAUSAL || (t * BN <= qw + 31); };
+    auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
     auto scores = [&](f32x16 (&s)[KB], const unsigned char* Ks) {
 #pragma unroll
@@ -167,20 +167,19 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
     float l = 0.f;         // running sum over this lane's keys (other half added at the end)
     const float c2 = a.c2;
 
-    // softmax of tile t held in s, then O^T += V_t^T P_t^T.
-    auto softmax_pv = [&](int t, f32x16 (&s)[KB]) {
-        const int j0 = t * BN;
-        // Tiles straddling the causal diagonal or the ragged end: masked
-        // scores become -inf (c2 > 0, so their exponentials are exactly 0).
-        const bool masked = (CAUSAL && j0 + BN - 1 > qw) || (j0 + BN > N);
-        if (masked) {
+    // Masking (tiles straddling the causal diagonal or the ragged end only:
+    // masked scores become -inf; c2 > 0, so their exponentials are exactly
+    // 0), row maximum and the lazy rescale of l and O for tile t in s.
+    auto prepare = [&](int t, f32x16 (&s)[KB], auto masked_c) {
+        if constexpr (decltype(masked_c)::value) {
+            // Key of element u of block kb is j0 + kb*32 + 4*hi + 8*(u/4) + u%4.
+            const int lim = CAUSAL ? min(N - 1, myq) : N - 1;   // last visible key
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb) {
+                const int thr = lim - (t * BN + kb * 32 + 4 * hi);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int key = j0 + kb * 32 + 8 * (u >> 2) + 4 * hi + (u & 3);
-                    if (key >= N || (CAUSAL && key > myq)) s[kb][u] = -INFINITY;
-                }
+                for (int u = 0; u < 16; ++u) s[kb][u] = (8 * (u >> 2) + (u & 3) > thr) ? -INFINITY : s[kb][u];
+            }
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -197,47 +196,81 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         }
+    };
 
-        // P^T as bf16 B operands: pb[kc] covers keys kc*16 .. kc*16+15 of the tile.
-        bf16x8 pb[BN / 16];
+    // One pipeline step, scheduled by hand (sched_barrier fences keep the
+    // order): while K_{t+2} and V_{t+1} stream into LDS, the 16 score MFMAs of
+    // tile t+1 are interleaved with the exponentials of tile t (phase A), then
+    // the PV MFMAs of tile t run (phase B). Operand reads run PFS / PFV MFMAs
+    // ahead. For the last tile the scores of a tile past the end are computed
+    // from stale LDS and never used.
+    constexpr int NS = KB * DC;           // score MFMAs per tile
+    constexpr int NP = DB * (BN / 16);    // PV MFMAs per tile
+    constexpr int EPS = KB * 16 / NS;     // exponentials per score MFMA
+    constexpr int PFS = 2;
+    constexpr int PFV = 2;
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    auto step = [&](int t, f32x16 (&scur)[KB], f32x16 (&snext)[KB], auto masked_c) {
+        if (t + 2 < ntiles) dma(Kg, t + 2, t & 1, false);
+        if (t + 1 < ntiles) dma(Vg, t + 1, 2 + ((t + 1) & 1), true);
+        prepare(t, scur, masked_c);
+        fence();
+
+        // Phase A. Score MFMA i: block i % KB, d chunk i / KB (two chains).
+        const unsigned char* Ks = kbuf((t + 1) & 1);
+        auto kread = [&](int i) {
+            return *reinterpret_cast<const bf16x8*>(Ks + (i % KB) * 32 * RB + (kbase ^ ((i / KB) << 5)));
+        };
+        bf16x8 kfr[NS];
+#pragma unroll
+        for (int i = 0; i < PFS; ++i) kfr[i] = kread(i);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) snext[kb] = f32x16{};
         float rowsum = 0.f;
+        u32x4 w[BN / 16];
+        bf16x8 pb[BN / 16];
+        fence();
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            float p[16];
+        for (int i = 0; i < NS; ++i) {
+            snext[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[i], qf[i / KB], snext[i % KB], 0, 0, 0);
+            if (i + PFS < NS) kfr[i + PFS] = kread(i + PFS);
+            // exponentials EPS*i .. EPS*i + EPS-1 of tile t (flat over blocks)
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                p[u] = exp2_fast(__builtin_fmaf(s[kb][u], c2, -m));
-                rowsum += p[u];
+            for (int e = 0; e < EPS; e += 2) {
+                const int f = EPS * i + e;
+                const int kb = f / 16, u = f % 16;
+                const float p0 = exp2_fast(__builtin_fmaf(scur[kb][u], c2, -m));
+                const float p1 = exp2_fast(__builtin_fmaf(scur[kb][u + 1], c2, -m));
+                rowsum += p0 + p1;
+                w[f / 8][(f % 8) / 2] = pack_bf16x2(p0, p1);
+                if (f % 8 == 6) pb[f / 8] = as_bf16x8(w[f / 8]);
             }
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                u32x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[half * 8 + 2 * e], p[half * 8 + 2 * e + 1]);
-                pb[kb * 2 + half] = as_bf16x8(w);
-            }
+            fence();
         }
         l += rowsum;
 
-        // V^T operand by transposing LDS reads of the row-major V tile.
+        // Phase B. PV MFMA j: key chunk j / DB, d block j % DB.
         const unsigned char* Vs = vbuf(t & 1);
+        auto vread = [&](int j) {
+            const int kc = j / DB, db = j % DB;
+            const int voff = (vbase ^ (db << 6)) + kc * 16 * RB;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vs + voff));
+            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vs + voff + 8 * RB));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 vfr[NP];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int voff = vbase ^ (db << 6);
+        for (int j = 0; j < PFV; ++j) vfr[j] = vread(j);
+        fence();
 #pragma unroll
-            for (int kc = 0; kc < BN / 16; ++kc) {
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16_t*)(Vs + kc * 16 * RB + voff));
-                const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16_t*)(Vs + (kc * 16 + 8) * RB + voff));
-                const v8i16 vv = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[kc],
-                                                                   oacc[db], 0, 0, 0);
-            }
+        for (int j = 0; j < NP; ++j) {
+            oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[j], pb[j / DB], oacc[j % DB], 0, 0, 0);
+            if (j + PFV < NP) vfr[j + PFV] = vread(j + PFV);
+            fence();
         }
+        wait_dma();
+        __syncthreads();
     };
-
-    auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
     // Prologue: K_0, V_0, K_1 into LDS, then S_0.
     dma(Kg, 0, 0, false);
@@ -249,19 +282,24 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
     scores(sa, kbuf(0));
     __syncthreads();   // Kbuf[0] receives K_2 in iteration 0
 
-    // One pipeline step: K_{t+2} and V_{t+1} stream into LDS while the scores
-    // of tile t+1 are multiplied and the softmax and PV of tile t run.
-    auto step = [&](int t, f32x16 (&scur)[KB], f32x16 (&snext)[KB]) {
-        if (t + 2 < ntiles) dma(Kg, t + 2, t & 1, false);
-        if (t + 1 < ntiles) dma(Vg, t + 1, 2 + ((t + 1) & 1), true);
-        if (t + 1 < ntiles && wave_active(t + 1)) scores(snext, kbuf((t + 1) & 1));
-        if (wave_active(t)) softmax_pv(t, scur);
-        wait_dma();
-        __syncthreads();
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, sa, sb);
-        if (t + 1 < ntiles) step(t + 1, sb, sa);
+    // Tiles before t_split need no mask for any wave (they end before the
+    // workgroup's first query and before N); the rest run the masked variant.
+    // Causal waves whose rows all precede a tile run it fully masked (p = 0).
+    const int t_split = min(CAUSAL ? q0 / BN : ntiles, (N % BN) ? ntiles - 1 : ntiles);
+    int t = 0;
+    for (; t + 1 < t_split; t += 2) {
+        step(t, sa, sb, std::false_type{});
+        step(t + 1, sb, sa, std::false_type{});
+    }
+    if (t < t_split) {
+        step(t, sa, sb, std::false_type{});
+        ++t;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
+    }
+    for (; t < ntiles; t += 2) {
+        step(t, sa, sb, std::true_type{});
+        if (t + 1 < ntiles) step(t + 1, sb, sa, std::true_type{});
     }
 
     // Epilogue: O = O^T / l (rounded to bf16), LSE = ln-domain m + ln l.
