@@ -75,15 +75,33 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 
 // Combine a per-lane value with the one held by lane (lane ^ 32): in the
 // 32x32 accumulator layout the two halves of a wave64 hold the same column.
+// v_permlane32_swap exchanges the upper 32 lanes of one operand with the
+// lower 32 lanes of the other; with x in both, each lane ends up holding x of
+// its own lane and of lane ^ 32, one in each result. It runs on the VALU (a
+// shuffle through ds_bpermute would count as an LDS access and wait for any
+// direct-to-LDS loads in flight). max and + are commutative, so both halves
+// get bit-identical results.
 __device__ __forceinline__ float max_halves(float x) {
-    return __builtin_fmaxf(x, __shfl_xor(x, 32));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float sum_halves(float x) {
-    return x + __shfl_xor(x, 32);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Materialises x in a VGPR at this point of the program: the computation of x
+// can no longer be sunk past it (the value itself is unchanged). Used to keep
+// running sums spread over a hand-scheduled loop instead of being gathered
+// into one serial chain at their first use.
+__device__ __forceinline__ void pin_vgpr(float& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(x));
+#endif
+}
 
 // Round-to-nearest-even fp32 pair -> packed bf16 pair (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

@@ -8,7 +8,7 @@
 //     score and probability matrices never reach HBM;
 //   * section "Tres mejoras en la utilización de la GPU": the grid covers
 //     (query block, head, batch), so a single long sequence still fills the
-//     chip; each wavefront owns its own 32 query rows and all four wavefronts
+//     chip; each wavefront owns its own 32 query rows and all eight wavefronts
 //     of a workgroup share the K/V tiles in LDS, so no partial output is ever
 //     exchanged between wavefronts; tiles entirely above the causal diagonal
 //     are never loaded, masking runs only on diagonal and ragged-tail tiles,
@@ -27,9 +27,9 @@
 //                 lane, so the online-softmax rescale is a per-lane scalar.
 //   Softmax in base 2: p = exp2(S * c2 - m) with c2 = |scale| * log2(e); a
 //   negative scale is folded into the sign bits of Q.
-//   K/V tiles are double-buffered in LDS: tile t+1 is fetched from HBM into
-//   registers (16-byte loads) while tile t is multiplied, then written to the
-//   other LDS buffer; one barrier per tile.
+//   K/V tiles are double-buffered in LDS and fetched by direct-to-LDS loads
+//   (global_load_lds, 16 bytes per lane) one step ahead of their use; one
+//   barrier per tile.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -114,16 +114,37 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
     // the tile; lane i writes LDS chunk slot i, so it fetches the global chunk
     // that the swizzle puts there. Rows past N are clamped to N-1 (they are
     // masked for K and meet P = 0 for V).
-    auto dma = [&](const __bf16* g, int t, int buf, bool is_v) {
+    // Element offsets of this lane's chunks within a tile (row * rs + chunk)
+    // are fixed; a whole tile adds a uniform t * BN * rs. Only the ragged
+    // last tile recomputes them with the clamp.
+    unsigned koff[IPW], voff[IPW];
 #pragma unroll
-        for (int j = 0; j < IPW; ++j) {
-            const int inst = wave + NW * j;
-            const int row = inst * RPI + lane / CPR;
-            const int slot = lane % CPR;
-            const int c = slot ^ (is_v ? swv(row) : swk(row));
-            const int grow = min(t * BN + row, N - 1);
-            __builtin_amdgcn_global_load_lds(g + (size_t)grow * rs + c * 8,
-                                             (lds_void_t*)(smem + buf * TILE + inst * 1024), 16, 0, 0);
+    for (int j = 0; j < IPW; ++j) {
+        const int row = (wave + NW * j) * RPI + lane / CPR;
+        const int slot = lane % CPR;
+        koff[j] = (unsigned)row * (unsigned)rs + 8u * (unsigned)(slot ^ swk(row));
+        voff[j] = (unsigned)row * (unsigned)rs + 8u * (unsigned)(slot ^ swv(row));
+    }
+    auto dma = [&](const __bf16* g, int t, int buf, bool is_v) {
+        if ((t + 1) * BN <= N) {
+            const __bf16* gt = g + (size_t)t * BN * rs;
+#pragma unroll
+            for (int j = 0; j < IPW; ++j) {
+                const int inst = wave + NW * j;
+                __builtin_amdgcn_global_load_lds(gt + (size_t)(is_v ? voff[j] : koff[j]),
+                                                 (lds_void_t*)(smem + buf * TILE + inst * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < IPW; ++j) {
+                const int inst = wave + NW * j;
+                const int row = inst * RPI + lane / CPR;
+                const int slot = lane % CPR;
+                const int c = slot ^ (is_v ? swv(row) : swk(row));
+                const int grow = min(t * BN + row, N - 1);
+                __builtin_amdgcn_global_load_lds(g + (size_t)grow * rs + c * 8,
+                                                 (lds_void_t*)(smem + buf * TILE + inst * 1024), 16, 0, 0);
+            }
         }
     };
     auto kbuf = [&](int i) { return smem + i * TILE; };
@@ -181,11 +202,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
                 for (int u = 0; u < 16; ++u) s[kb][u] = (8 * (u >> 2) + (u & 3) > thr) ? -INFINITY : s[kb][u];
             }
         }
-        float mx = -INFINITY;
+        // Four independent max chains instead of one serial chain.
+        float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int u = 0; u < 16; ++u) mx = __builtin_fmaxf(mx, s[kb][u]);
+            for (int u = 0; u < 16; u += 2)
+                mc[(u / 2) % 4] = __builtin_fmaxf(__builtin_fmaxf(mc[(u / 2) % 4], s[kb][u]), s[kb][u + 1]);
+        float mx = __builtin_fmaxf(__builtin_fmaxf(mc[0], mc[1]), __builtin_fmaxf(mc[2], mc[3]));
         mx = max_halves(mx);
         const float mt = mx * c2;   // -inf when every key of the row is masked in this tile
         if (__builtin_amdgcn_ballot_w64(mt > m + kTau) != 0) {
@@ -200,54 +224,96 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
 
     // One pipeline step, scheduled by hand (sched_barrier fences keep the
     // order): while K_{t+2} and V_{t+1} stream into LDS, the 16 score MFMAs of
-    // tile t+1 are interleaved with the exponentials of tile t (phase A), then
-    // the PV MFMAs of tile t run (phase B). Operand reads run PFS / PFV MFMAs
-    // ahead. For the last tile the scores of a tile past the end are computed
-    // from stale LDS and never used.
+    // tile t+1 are interleaved with the exponentials of tile t (phase A, run
+    // at raised wave priority so that the VALU-heavy phase of one wave is
+    // not starved by the other wave's PV MFMAs), then the PV MFMAs of tile t
+    // run (phase B). K operands are read in batches of KBS MFMAs one batch
+    // ahead (while a direct-to-LDS load is in flight the compiler can only
+    // wait for all outstanding LDS reads, so reads issued one MFMA ahead
+    // would be waited for at once); V operands PFV MFMAs ahead. For the last
+    // tile the scores of a tile past the end are computed from stale LDS and
+    // never used.
     constexpr int NS = KB * DC;           // score MFMAs per tile
     constexpr int NP = DB * (BN / 16);    // PV MFMAs per tile
-    constexpr int EPS = KB * 16 / NS;     // exponentials per score MFMA
-    constexpr int PFS = 2;
+    constexpr int KBS = 2;
     constexpr int PFV = 2;
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
     auto step = [&](int t, f32x16 (&scur)[KB], f32x16 (&snext)[KB], auto masked_c) {
         if (t + 2 < ntiles) dma(Kg, t + 2, t & 1, false);
         if (t + 1 < ntiles) dma(Vg, t + 1, 2 + ((t + 1) & 1), true);
-        prepare(t, scur, masked_c);
-        fence();
-
         // Phase A. Score MFMA i: block i % KB, d chunk i / KB (two chains).
+        // K operands are read in batches of KBS MFMAs, one batch ahead; the
+        // first batch is in flight during prepare.
         const unsigned char* Ks = kbuf((t + 1) & 1);
         auto kread = [&](int i) {
             return *reinterpret_cast<const bf16x8*>(Ks + (i % KB) * 32 * RB + (kbase ^ ((i / KB) << 5)));
         };
         bf16x8 kfr[NS];
 #pragma unroll
-        for (int i = 0; i < PFS; ++i) kfr[i] = kread(i);
+        for (int i = 0; i < KBS; ++i) kfr[i] = kread(i);
+        fence();
+        prepare(t, scur, masked_c);
+        fence();
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) snext[kb] = f32x16{};
-        float rowsum = 0.f;
+        // Two partial row sums; each partial is pinned in place after its add
+        // so that the adds stay spread over phase A instead of being sunk to
+        // the end of the step as one serial chain.
+        float rsum[2] = {0.f, 0.f};
         u32x4 w[BN / 16];
         bf16x8 pb[BN / 16];
+        // The exponentials of tile t run as a three-stage pipeline over the
+        // score MFMAs, so that no slot waits on a result produced in the same
+        // slot: pair q (elements 2q, 2q+1 flat over blocks) gets its fma two
+        // slots ahead, its exp2 one slot ahead and its sum / bf16 pack in
+        // slot q / PPS.
+        constexpr int NPAIR = KB * 8;
+        constexpr int PPS = NPAIR / NS;       // pairs per score MFMA
+        static_assert(PPS * NS == NPAIR && PPS >= 1, "pairs must split evenly over the MFMAs");
+        float x[NPAIR][2], e[NPAIR][2];
+        auto valu_slot = [&](int i) {
+#pragma unroll
+            for (int q = (i + 2) * PPS; q < (i + 3) * PPS; ++q) {
+                if (q < 0 || q >= NPAIR) continue;
+                const int f = 2 * q, kb = f / 16, u = f % 16;
+                x[q][0] = __builtin_fmaf(scur[kb][u], c2, -m);
+                x[q][1] = __builtin_fmaf(scur[kb][u + 1], c2, -m);
+            }
+#pragma unroll
+            for (int q = (i + 1) * PPS; q < (i + 2) * PPS; ++q) {
+                if (q < 0 || q >= NPAIR) continue;
+                e[q][0] = exp2_fast(x[q][0]);
+                e[q][1] = exp2_fast(x[q][1]);
+                pin_vgpr(e[q][0]);
+                pin_vgpr(e[q][1]);
+            }
+#pragma unroll
+            for (int q = i * PPS; q < (i + 1) * PPS; ++q) {
+                if (q < 0 || q >= NPAIR) continue;
+                const int f = 2 * q;
+                rsum[q % 2] += e[q][0] + e[q][1];
+                pin_vgpr(rsum[q % 2]);
+                w[f / 8][(f % 8) / 2] = pack_bf16x2(e[q][0], e[q][1]);
+                if (f % 8 == 6) pb[f / 8] = as_bf16x8(w[f / 8]);
+            }
+        };
+        __builtin_amdgcn_s_setprio(1);
+        valu_slot(-2);
+        fence();
+        valu_slot(-1);
         fence();
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             snext[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[i], qf[i / KB], snext[i % KB], 0, 0, 0);
-            if (i + PFS < NS) kfr[i + PFS] = kread(i + PFS);
-            // exponentials EPS*i .. EPS*i + EPS-1 of tile t (flat over blocks)
+            fence();
+            if (i % KBS == 0) {
 #pragma unroll
-            for (int e = 0; e < EPS; e += 2) {
-                const int f = EPS * i + e;
-                const int kb = f / 16, u = f % 16;
-                const float p0 = exp2_fast(__builtin_fmaf(scur[kb][u], c2, -m));
-                const float p1 = exp2_fast(__builtin_fmaf(scur[kb][u + 1], c2, -m));
-                rowsum += p0 + p1;
-                w[f / 8][(f % 8) / 2] = pack_bf16x2(p0, p1);
-                if (f % 8 == 6) pb[f / 8] = as_bf16x8(w[f / 8]);
+                for (int r = i + KBS; r < i + 2 * KBS && r < NS; ++r) kfr[r] = kread(r);
             }
+            valu_slot(i);
             fence();
         }
-        l += rowsum;
+        l += rsum[0] + rsum[1];
 
         // Phase B. PV MFMA j: key chunk j / DB, d block j % DB.
         const unsigned char* Vs = vbuf(t & 1);
@@ -262,6 +328,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < PFV; ++j) vfr[j] = vread(j);
         fence();
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[j], pb[j / DB], oacc[j % DB], 0, 0, 0);
