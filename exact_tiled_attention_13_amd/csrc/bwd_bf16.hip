@@ -143,11 +143,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int trb1 = T::trbase(lane, 1);
 
     auto stage_ptr = [&](int s) { return smem + s * STAGE; };
+    unsigned toff[T::NINST / NW];
+    T::template offsets<NW>(toff, rs, wave, lane);
     auto dma = [&](int t, int s) {
         unsigned char* st = stage_ptr(s);
         const int q0 = qstart + t * BQ;
-        T::template load<NW>(st, Qg, rs, q0, N, wave, lane);
-        T::template load<NW>(st + T::BYTES, dOg, rs, q0, N, wave, lane);
+        T::template load<NW>(st, Qg, rs, q0, N, wave, lane, toff);
+        T::template load<NW>(st + T::BYTES, dOg, rs, q0, N, wave, lane, toff);
         // q0 + 63 < npad: the padded statistics need no clamp.
         if (wave == 0)
             __builtin_amdgcn_global_load_lds(lsg + q0 + lane, (lds_void_t*)(st + 2 * T::BYTES), 4, 0, 0);
@@ -392,9 +394,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
 
     auto kbuf = [&](int s) { return smem + s * T::BYTES; };
     auto vbuf = [&](int s) { return smem + (2 + s) * T::BYTES; };
+    unsigned toff[T::NINST / NW];
+    T::template offsets<NW>(toff, rs, wave, lane);
     auto dma = [&](int t, int s) {
-        T::template load<NW>(kbuf(s), Kg, rs, t * BN, N, wave, lane);
-        T::template load<NW>(vbuf(s), Vg, rs, t * BN, N, wave, lane);
+        T::template load<NW>(kbuf(s), Kg, rs, t * BN, N, wave, lane, toff);
+        T::template load<NW>(vbuf(s), Vg, rs, t * BN, N, wave, lane, toff);
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 

@@ -33,21 +33,43 @@ struct LdsTile {
         return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
     }
 
-    // Wave `w` of NW loads its share of rows row0 .. row0+63 of g (row
-    // stride rs elements) into the tile at `dst`. Rows at or past n are
-    // clamped to n - 1: callers mask them.
+    // Element offsets (tile row * rs + chunk) of the chunks that lane `lane`
+    // of wave `w` (of NW) fetches; they are the same for every tile, so a
+    // kernel computes them once.
     template <int NW>
-    __device__ static __forceinline__ void load(unsigned char* dst, const __bf16* g, size_t rs, int row0, int n,
-                                                int w, int lane) {
+    __device__ static __forceinline__ void offsets(unsigned (&off)[NINST / NW], size_t rs, int w, int lane) {
         static_assert(NINST % NW == 0, "tile loads must split evenly over the waves");
 #pragma unroll
         for (int j = 0; j < NINST / NW; ++j) {
-            const int inst = w + NW * j;
-            const int row = inst * RPI + lane / CPR;
+            const int row = (w + NW * j) * RPI + lane / CPR;
             const int c = (lane % CPR) ^ swz(row);
-            const int grow = min(row0 + row, n - 1);
-            __builtin_amdgcn_global_load_lds(g + (size_t)grow * rs + c * 8, (lds_void_t*)(dst + inst * 1024), 16,
-                                             0, 0);
+            off[j] = (unsigned)row * (unsigned)rs + 8u * (unsigned)c;
+        }
+    }
+
+    // Wave `w` of NW loads its share of rows row0 .. row0+63 of g (row
+    // stride rs elements) into the tile at `dst`; `off` comes from offsets().
+    // Rows at or past n are clamped to n - 1: callers mask them. Full tiles
+    // only add the uniform row0 * rs to the precomputed offsets.
+    template <int NW>
+    __device__ static __forceinline__ void load(unsigned char* dst, const __bf16* g, size_t rs, int row0, int n,
+                                                int w, int lane, const unsigned (&off)[NINST / NW]) {
+        if (row0 + ROWS <= n) {
+            const __bf16* gt = g + (size_t)row0 * rs;
+#pragma unroll
+            for (int j = 0; j < NINST / NW; ++j)
+                __builtin_amdgcn_global_load_lds(gt + (size_t)off[j], (lds_void_t*)(dst + (w + NW * j) * 1024), 16,
+                                                 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NINST / NW; ++j) {
+                const int inst = w + NW * j;
+                const int row = inst * RPI + lane / CPR;
+                const int c = (lane % CPR) ^ swz(row);
+                const int grow = min(row0 + row, n - 1);
+                __builtin_amdgcn_global_load_lds(g + (size_t)grow * rs + c * 8, (lds_void_t*)(dst + inst * 1024),
+                                                 16, 0, 0);
+            }
         }
     }
 
