@@ -99,6 +99,44 @@ def cpu_baseline(q, k, v, do, scale, heads=2):
     }
 
 
+def time_passes(w, reps=10, warmup=3):
+    """Report-only timing of one workload: forward (and backward, when the
+    workload has one) for each of its masks, HIP events around `reps`
+    back-to-back launches after `warmup` untimed ones."""
+    import torch
+
+    import exact_tiled_attention_13_amd as fa
+    from exact_tiled_attention_13_amd.inputs import make_workload
+
+    dev = torch.device("cuda:0")
+    xs = [x.to(dev) for x in make_workload(w)]
+    q, k, v = xs[:3]
+    out = {}
+    for c in w.causal:
+        tag = "causal" if c else "noncausal"
+        o, lse = fa.attn_fwd(q, k, v, c, w.scale)
+        calls = {"fwd": (lambda: fa.attn_fwd(q, k, v, c, w.scale, o=o, lse=lse), 1.0)}
+        if w.backward:
+            ws = fa.workspace(w.B, w.H, w.N, w.d, dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            calls["bwd"] = (lambda: fa.attn_bwd(q, k, v, o, xs[3], lse, c, w.scale, dq=dq, dk=dk, dv=dv,
+                                                workspace=ws), 2.5)
+        for name, (f, mult) in calls.items():
+            for _ in range(warmup):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            flop = mult * counted_fwd(w.B, w.H, w.N, w.d, c)
+            out[f"{name}_{tag}"] = {"ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                                    "frac_bf16_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +279,14 @@ def main():
         "gpu": torch.cuda.get_device_name(dev),
         "max_memory_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
     }
+    # Report-only: the other 16k-token workloads (head dim 64 at 16k tokens,
+    # the short-sequence and mid-length configurations, the batched backward).
+    from exact_tiled_attention_13_amd.inputs import LONG_D64, WORKLOADS
+
+    report = {LONG_D64.name: time_passes(LONG_D64)}
+    for name in ("fwd_bf16_b32_h32_n512_d64", "fwd_bf16_b8_h16_n2048_d128", "bwd_bf16_b4_h16_n4096_d128"):
+        report[name] = time_passes(WORKLOADS[name])
+    out["other_workloads"] = report
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale)
     print(json.dumps(out), flush=True)

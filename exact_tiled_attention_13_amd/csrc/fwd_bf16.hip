@@ -364,9 +364,27 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
     }
+    // Under the causal mask a wave stops computing at the first tile whose
+    // keys all follow its last query (that tile and every later one give
+    // p = 0), but keeps issuing its share of the loads and passing the
+    // barriers until the workgroup is done.
+    auto idle = [&](int tt) { return CAUSAL && tt * BN > qw + 31; };
     for (; t < ntiles; t += 2) {
+        if (idle(t)) break;
         step(t, sa, sb, std::true_type{});
-        if (t + 1 < ntiles) step(t + 1, sb, sa, std::true_type{});
+        if (t + 1 < ntiles) {
+            if (idle(t + 1)) {
+                ++t;
+                break;
+            }
+            step(t + 1, sb, sa, std::true_type{});
+        }
+    }
+    for (; t < ntiles; ++t) {
+        if (t + 2 < ntiles) dma(Kg, t + 2, t & 1, false);
+        if (t + 1 < ntiles) dma(Vg, t + 1, 2 + ((t + 1) & 1), true);
+        wait_dma();
+        __syncthreads();
     }
 
     // Epilogue: O = O^T / l (rounded to bf16), LSE = ln-domain m + ln l.

@@ -61,6 +61,10 @@ WORKLOADS = {
 # Backward timed at the long-context shape (batch 1, 16 heads, 16k tokens, d 128).
 BWD_LONG = Workload("bwd_bf16_b1_h16_n16384_d128", "bf16", 1, 16, 16384, 128, (False, True), True, 1004)
 
+# The head-dim-64 point of the same 16k-token sweep at its longest sequence
+# (H * d = 2048 as in every other workload); reported beside the main step.
+LONG_D64 = Workload("bwd_bf16_b1_h32_n16384_d64", "bf16", 1, 32, 16384, 64, (False, True), True, 1006)
+
 
 def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0, with_do: bool = False):
     """Draw Q, K, V (and dO) on the CPU. Returns a tuple of CPU tensors [B, N, H, d].
