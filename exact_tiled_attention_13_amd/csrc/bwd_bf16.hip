@@ -523,13 +523,15 @@ static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
     // 4-wave workgroups (two per CU) for d = 64 and for d = 128 up to 2048
     // tokens, as in the forward (measured: 5-26% faster there; 8 waves win
     // for d = 128 from 4096 tokens on).
-    if (D == 64 || a.N <= 2048) {
-        const long long g = (long long)((a.N + 127) / 128) * a.B * a.H;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 4>), dim3((unsigned)g), dim3(256), 0, stream, a);
-        return hipGetLastError();
+    if constexpr (D == 128) {
+        if (a.N > 2048) {
+            const long long g = (long long)((a.N + 255) / 256) * a.B * a.H;
+            hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 8>), dim3((unsigned)g), dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
     }
-    const long long g = (long long)((a.N + 255) / 256) * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 8>), dim3((unsigned)g), dim3(512), 0, stream, a);
+    const long long g = (long long)((a.N + 127) / 128) * a.B * a.H;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 4>), dim3((unsigned)g), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -418,13 +418,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    if (D == 64 || a.N <= kFwdShortN) {
-        const long long grid = (long long)((a.N + 127) / 128) * a.B * a.H;
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a);
-    } else {
-        const long long grid = (long long)((a.N + 255) / 256) * a.B * a.H;
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+    if constexpr (D == 128) {
+        if (a.N > kFwdShortN) {
+            const long long grid = (long long)((a.N + 255) / 256) * a.B * a.H;
+            hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
     }
+    const long long grid = (long long)((a.N + 127) / 128) * a.B * a.H;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -153,6 +153,24 @@ def test_bwd_bf16_other_scales(scale):
         assert nerr(f64(dv), rv) <= TOL_GRAD_BF16
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_bwd_bf16_ragged_long_d128(causal):
+    """Head dim 128 beyond 2048 tokens runs the 8-wave forward and dQ
+    kernels (shorter sequences and d = 64 run the 4-wave ones); a ragged
+    length (2113 = 33 * 64 + 1) checks their tail handling."""
+    N = 2113
+    q, k, v, do = make_qkv(1, 2, N, 128, "bf16", seed=2113 + causal, with_do=True)
+    s = float(np.float32(128 ** -0.5))
+    o, lse, dq, dk, dv = run_bwd(q, k, v, do, causal, s)
+    ro, rl = attn_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, s)
+    assert nerr(f64(o), ro) <= TOL_O_BF16
+    assert aerr(f64(lse), rl) <= TOL_LSE_BF16
+    rq, rk, rv = attn_bwd(*(x.double().numpy() for x in (q, k, v, do)), causal, s)
+    assert nerr(f64(dq), rq) <= TOL_GRAD_BF16
+    assert nerr(f64(dk), rk) <= TOL_GRAD_BF16
+    assert nerr(f64(dv), rv) <= TOL_GRAD_BF16
+
+
 def test_bwd_bf16_workload_n4096_sampled_heads():
     """4 x 16 heads x 4096 tokens, d 128, causal: O and LSE from the forward
     kernel feed the backward; three whole heads are checked against the oracle."""
