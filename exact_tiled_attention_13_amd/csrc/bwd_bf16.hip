@@ -22,7 +22,7 @@
 // and causal tiles that are entirely masked are skipped.
 //
 // Workspace: two fp32 arrays [B, H, Npad] (Npad = 64 * ceil(N / 64)), first
-// D_i, then LSE_i * log2(e); padded rows hold D = 0 and LSE = +inf, so their
+// -D_i, then LSE_i * log2(e); padded rows hold D = 0 and LSE = +inf, so their
 // probabilities are exactly 0.
 #include <type_traits>
 
@@ -32,7 +32,9 @@
 
 namespace fa {
 
-// D_i = sum_c dO[b,i,h,c] * O[b,i,h,c] and LSE_i * log2(e), fp32 [B, H, Npad].
+// -D_i = -sum_c dO[b,i,h,c] * O[b,i,h,c] and LSE_i * log2(e), fp32 [B, H, Npad].
+// D is stored negated so that the dK/dV kernel can start its dP accumulator
+// at -D (dP - D then comes out of the MFMAs) and the dQ kernel adds it.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     constexpr int TPR = D / 8;               // threads per row (8 elements each)
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (r < rows && c == 0) {
         const long long i = (b * a.H + h) * npad + n;
-        a.dd[i] = real ? acc : 0.f;
+        a.dd[i] = real ? -acc : 0.f;
         a.lse2[i] = real ? a.lse[(b * a.H + h) * a.N + n] * kLog2e : INFINITY;
     }
 }
@@ -182,7 +184,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             const int g4 = k;
             const int ql = mb * 32 + 8 * g4 + 4 * hi;   // tile-local query of element 4*g4
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int u = 4 * g4 + e;
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                 // the diagonal).
                 if constexpr (MASKED) sv = (thr > 8 * g4 + e) ? -INFINITY : sv;
                 x.p[u] = exp2_fast(__builtin_fmaf(sv, c2, -l4[e]));
-                x.ds[u] = x.p[u] * (x.dp[u] - d4[e]);
+                x.ds[u] = x.p[u] * x.dp[u];   // dP accumulator started at -D
             }
         } else {
             const int half = k - 4;
@@ -233,8 +234,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             Soft& y = x[i / DC];
             const int cc = i % DC;
             if (cc == 0) {
+                // dP - D: the accumulator starts at -D of its 16 query rows
+                // (element u is query 8*(u/4) + 4*hi + u%4 of the block).
                 y.s = f32x16{};
-                y.dp = f32x16{};
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + (i / DC) * 32 + 8 * g4 + 4 * hi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y.dp[4 * g4 + e] = d4[e];
+                }
             }
             y.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i], kf[cc], y.s, 0, 0, 0);
             y.dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[i], vf[cc], y.dp, 0, 0, 0);
@@ -378,7 +386,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
         gf[c] = as_bf16x8(gv);
     }
     const float lse2 = (myq < N) ? a.lse2[(size_t)bh * npad + myq] : 0.f;
-    const float dd = (myq < N) ? a.dd[(size_t)bh * npad + myq] : 0.f;
+    const float ndd = (myq < N) ? a.dd[(size_t)bh * npad + myq] : 0.f;   // -D of this lane's query
 
     f32x16 dqacc[DB];
 #pragma unroll
@@ -440,7 +448,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
             }
             float ds[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) ds[u] = exp2_fast(__builtin_fmaf(s[u], c2, -lse2)) * (dp[u] - dd);
+            for (int u = 0; u < 16; ++u) ds[u] = exp2_fast(__builtin_fmaf(s[u], c2, -lse2)) * (dp[u] + ndd);
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 u32x4 w;

@@ -95,7 +95,8 @@ int attn_fwd_fp32(const float* q, const float* k, const float* v, float* o, floa
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for this
  * shape: two fp32 arrays [B, H, Npad] with Npad = 64 * ceil(N / 64), the row
- * statistics D_i = dO_i . O_i and LSE_i * log2(e), rounded up to 256 bytes.
+ * statistics -D_i (D_i = dO_i . O_i) and LSE_i * log2(e), rounded up to 256
+ * bytes.
  * Returns 0 for arguments attn_bwd would reject.
  */
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, int causal);
@@ -126,13 +127,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * so that a caller can time or schedule them separately; attn_bwd is exactly
  * attn_bwd_prep, then attn_bwd_dkdv, then attn_bwd_dq on the same workspace.
  *
- * attn_bwd_prep -- fills the workspace: D_i = sum_c dO[b, i, h, c] * O[b, i, h, c]
- *   (the row statistic sum_j P_ij dP_ij of the softmax backward) and
- *   LSE_i * log2(e), fp32, with D = 0 and LSE = +inf on the padded rows.
+ * attn_bwd_prep -- fills the workspace: -D_i, where D_i = sum_c dO[b, i, h, c] *
+ *   O[b, i, h, c] (the row statistic sum_j P_ij dP_ij of the softmax
+ *   backward), then LSE_i * log2(e), fp32, with D = 0 and LSE = +inf on the
+ *   padded rows.
  * attn_bwd_dkdv -- dk = scale * dS^T Q and dv = P^T dO: one workgroup per
  *   block of 128 keys, looping over query tiles; reads the workspace.
- * attn_bwd_dq -- dq = scale * dS K: one workgroup per block of 256 queries,
- *   looping over key tiles (recomputes P and dP); reads the workspace.
+ * attn_bwd_dq -- dq = scale * dS K: one workgroup per block of 256 queries
+ *   (128 for d = 64 or N <= 2048), looping over key tiles (recomputes P and
+ *   dP); reads the workspace.
  * Arguments and errors as for attn_bwd.
  */
 int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace, size_t workspace_bytes,
