@@ -12,7 +12,7 @@ the average duration of every kernel is measured inside the timed region;
 the dominant one is reported against its roofline. The fp64 CPU oracle is
 timed on a bounded sample of the same workload as a reported baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-report]
 """
 
 from __future__ import annotations
@@ -143,6 +143,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-report", action="store_true", help="skip the report-only timings of the other workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -283,10 +284,11 @@ def main():
     # the short-sequence and mid-length configurations, the batched backward).
     from exact_tiled_attention_13_amd.inputs import LONG_D64, WORKLOADS
 
-    report = {LONG_D64.name: time_passes(LONG_D64)}
-    for name in ("fwd_bf16_b32_h32_n512_d64", "fwd_bf16_b8_h16_n2048_d128", "bwd_bf16_b4_h16_n4096_d128"):
-        report[name] = time_passes(WORKLOADS[name])
-    out["other_workloads"] = report
+    if not args.no_report:
+        report = {LONG_D64.name: time_passes(LONG_D64)}
+        for name in ("fwd_bf16_b32_h32_n512_d64", "fwd_bf16_b8_h16_n2048_d128", "bwd_bf16_b4_h16_n4096_d128"):
+            report[name] = time_passes(WORKLOADS[name])
+        out["other_workloads"] = report
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale)
     print(json.dumps(out), flush=True)
