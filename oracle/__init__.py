@@ -27,6 +27,10 @@ Modules:
   describe, plus the per-block-normalised negative control.
 * :mod:`oracle.brute` -- scalar-loop brute force for tiny inputs, written by a
   different algebraic route, used only to pin :mod:`oracle.attn_ref`.
+* :mod:`oracle.gqa` -- grouped-query / multi-query attention (K and V shared
+  by groups of query heads; page "FlashAttention-T: Optimización GPU para
+  LLMs Escalables", section "Innovaciones técnicas frente a FlashAttention
+  original"), defined head by head through :mod:`oracle.attn_ref`.
 
 Every function is pinned by ``tests/test_oracle*.py`` (brute force, torch CPU
 fp64 library routines, closed forms, invariants, finite differences and the
@@ -43,3 +47,4 @@ from .attn_ref import (  # noqa: F401
     flops_fwd,
     flops_bwd,
 )
+from .gqa import attn_bwd_gqa, attn_fwd_gqa  # noqa: F401
