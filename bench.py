@@ -112,15 +112,18 @@ def time_passes(w, reps=10, warmup=3):
     xs = [x.to(dev) for x in make_workload(w)]
     q, k, v = xs[:3]
     out = {}
+    gqa = w.kv_heads != w.H
+    fwd = fa.attn_fwd_gqa if gqa else fa.attn_fwd
+    bwd = fa.attn_bwd_gqa if gqa else fa.attn_bwd
     for c in w.causal:
         tag = "causal" if c else "noncausal"
-        o, lse = fa.attn_fwd(q, k, v, c, w.scale)
-        calls = {"fwd": (lambda: fa.attn_fwd(q, k, v, c, w.scale, o=o, lse=lse), 1.0)}
+        o, lse = fwd(q, k, v, c, w.scale)
+        calls = {"fwd": (lambda: fwd(q, k, v, c, w.scale, o=o, lse=lse), 1.0)}
         if w.backward:
             ws = fa.workspace(w.B, w.H, w.N, w.d, dev)
             dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-            calls["bwd"] = (lambda: fa.attn_bwd(q, k, v, o, xs[3], lse, c, w.scale, dq=dq, dk=dk, dv=dv,
-                                                workspace=ws), 2.5)
+            calls["bwd"] = (lambda: bwd(q, k, v, o, xs[3], lse, c, w.scale, dq=dq, dk=dk, dv=dv,
+                                        workspace=ws), 2.5)
         for name, (f, mult) in calls.items():
             for _ in range(warmup):
                 f()
@@ -281,11 +284,12 @@ def main():
         "max_memory_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
     }
     # Report-only: the other 16k-token workloads (head dim 64 at 16k tokens,
-    # the short-sequence and mid-length configurations, the batched backward).
-    from exact_tiled_attention_13_amd.inputs import LONG_D64, WORKLOADS
+    # grouped-query attention at 16k tokens, the short-sequence and mid-length
+    # configurations, the batched backward).
+    from exact_tiled_attention_13_amd.inputs import LONG_D64, LONG_GQA, WORKLOADS
 
     if not args.no_report:
-        report = {LONG_D64.name: time_passes(LONG_D64)}
+        report = {LONG_D64.name: time_passes(LONG_D64), LONG_GQA.name: time_passes(LONG_GQA)}
         for name in ("fwd_bf16_b32_h32_n512_d64", "fwd_bf16_b8_h16_n2048_d128", "bwd_bf16_b4_h16_n4096_d128"):
             report[name] = time_passes(WORKLOADS[name])
         out["other_workloads"] = report

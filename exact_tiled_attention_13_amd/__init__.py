@@ -18,10 +18,12 @@ from ._binding import (  # noqa: F401
     attn_bwd,
     attn_bwd_dkdv,
     attn_bwd_dq,
+    attn_bwd_gqa,
     attn_bwd_prep,
     attn_bwd_workspace_size,
     attn_fwd,
     attn_fwd_fp32,
+    attn_fwd_gqa,
     default_scale,
     lib,
     status_string,

@@ -24,7 +24,7 @@ FA_ERR_WORKSPACE = 3
 FA_ERR_HIP = 4
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_prep",
-            "attn_bwd_dkdv", "attn_bwd_dq", "fa_status_string")
+            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_gqa", "attn_bwd_gqa", "fa_status_string")
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
             L.attn_bwd_dkdv.restype = ci
             L.attn_bwd_dq.argtypes = [vp] * 5 + [sz, vp, ci, ci, ci, ci, ci, cf, vp]
             L.attn_bwd_dq.restype = ci
+            L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
+            L.attn_fwd_gqa.restype = ci
+            L.attn_bwd_gqa.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, ci, cf, vp]
+            L.attn_bwd_gqa.restype = ci
             L.fa_status_string.argtypes = [ci]
             L.fa_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -217,3 +221,53 @@ def attn_bwd_dq(q, k, v, do, ws, causal: bool = False, scale: float | None = Non
     _check("attn_bwd_dq", lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(ws), _nbytes(ws), _ptr(dq),
                                             B, H, N, d, int(bool(causal)), s, _stream(dev)))
     return dq
+
+
+def _kv_heads(q, k):
+    B, N, H, d = _shape(q)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+        raise ValueError(f"k: expected [B, N, Hkv, d] = [{B}, {N}, Hkv, {d}], got {tuple(k.shape)}")
+    return B, N, H, int(k.shape[2]), d
+
+
+def attn_fwd_gqa(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None):
+    """Grouped-query forward: q [B, N, H, d], k, v [B, N, Hkv, d] bf16 (H a multiple of Hkv). Returns (o, lse)."""
+    B, N, H, Hkv, d = _kv_heads(q, k)
+    dev = q.device
+    _expect("q", q, (B, N, H, d), torch.bfloat16, dev)
+    for name, t in (("k", k), ("v", v)):
+        _expect(name, t, (B, N, Hkv, d), torch.bfloat16, dev)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _expect("o", o, (B, N, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    s = default_scale(d) if scale is None else float(scale)
+    _check("attn_fwd_gqa", lib().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                                              int(bool(causal)), s, _stream(dev)))
+    return o, lse
+
+
+def attn_bwd_gqa(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+                 dq=None, dk=None, dv=None, workspace=None):
+    """Grouped-query backward. Returns (dq [B, N, H, d], dk, dv [B, N, Hkv, d]), bf16."""
+    B, N, H, Hkv, d = _kv_heads(q, k)
+    dev = q.device
+    for name, t in (("q", q), ("o", o), ("do", do)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    for name, t in (("k", k), ("v", v)):
+        _expect(name, t, (B, N, Hkv, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _expect("dq", dq, (B, N, H, d), torch.bfloat16, dev)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _expect(name, t, (B, N, Hkv, d), torch.bfloat16, dev)
+    need = attn_bwd_workspace_size(B, H, N, d, causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    s = default_scale(d) if scale is None else float(scale)
+    _check("attn_bwd_gqa", lib().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                              _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace), B, H, Hkv,
+                                              N, d, int(bool(causal)), s, _stream(dev)))
+    return dq, dk, dv

@@ -26,6 +26,11 @@ int check_shape(int B, int H, int N, int d, float scale) {
     return FA_OK;
 }
 
+int check_heads(int H, int Hkv) {
+    if (Hkv <= 0 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
 int check_ptrs(std::initializer_list<const void*> ps) {
     for (const void* p : ps)
         if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
@@ -58,17 +63,24 @@ int check_ws(const void* ws, size_t bytes, int B, int H, int N) {
 
 extern "C" {
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-             int causal, float scale, hipStream_t stream) {
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                 int d, int causal, float scale, hipStream_t stream) {
     int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_heads(H, Hkv);
     if (st != FA_OK) return st;
     st = check_ptrs({q, k, v, o, lse});
     if (st != FA_OK) return st;
     fa::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.B = B; a.H = H; a.N = N;
+    a.B = B; a.H = H; a.N = N; a.Hkv = Hkv;
     fill_scale(scale, a.c2, a.qsign, a.qsign_f);
     return fa::launch_fwd_bf16(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+             int causal, float scale, hipStream_t stream) {
+    return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
 }
 
 int attn_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
@@ -79,7 +91,7 @@ int attn_fwd_fp32(const float* q, const float* k, const float* v, float* o, floa
     if (st != FA_OK) return st;
     fa::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.B = B; a.H = H; a.N = N;
+    a.B = B; a.H = H; a.N = N; a.Hkv = H;
     fill_scale(scale, a.c2, a.qsign, a.qsign_f);
     return fa::launch_fwd_fp32(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -102,15 +114,17 @@ int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspa
     a.o = o; a.dO = dO; a.lse = lse;
     a.dd = static_cast<float*>(workspace);
     a.lse2 = a.dd + ws_half_elems(B, H, N);
-    a.B = B; a.H = H; a.N = N;
+    a.B = B; a.H = H; a.N = N; a.Hkv = H;
     return fa::launch_bwd_prep(a, d, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 namespace {
 
 int fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* dO, const void* workspace,
-             size_t workspace_bytes, int B, int H, int N, int d, float scale) {
+             size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale) {
     int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_heads(H, Hkv);
     if (st != FA_OK) return st;
     st = check_ptrs({q, k, v, dO});
     if (st != FA_OK) return st;
@@ -119,20 +133,18 @@ int fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const 
     a.q = q; a.k = k; a.v = v; a.dO = dO;
     a.dd = static_cast<float*>(const_cast<void*>(workspace));
     a.lse2 = a.dd + ws_half_elems(B, H, N);
-    a.B = B; a.H = H; a.N = N;
+    a.B = B; a.H = H; a.N = N; a.Hkv = Hkv;
     a.scale = scale;
     float unused;
     fill_scale(scale, a.c2, a.qsign, unused);
     return FA_OK;
 }
 
-}  // namespace
-
-int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
-                  size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
-                  hipStream_t stream) {
+int dkdv_stage(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+               size_t workspace_bytes, void* dk, void* dv, int B, int H, int Hkv, int N, int d, int causal,
+               float scale, hipStream_t stream) {
     fa::BwdArgs a{};
-    int st = fill_bwd(a, q, k, v, dO, workspace, workspace_bytes, B, H, N, d, scale);
+    int st = fill_bwd(a, q, k, v, dO, workspace, workspace_bytes, B, H, Hkv, N, d, scale);
     if (st != FA_OK) return st;
     st = check_ptrs({dk, dv});
     if (st != FA_OK) return st;
@@ -140,11 +152,11 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, c
     return fa::launch_bwd_dkdv(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
-                size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal, float scale,
-                hipStream_t stream) {
+int dq_stage(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+             size_t workspace_bytes, void* dq, int B, int H, int Hkv, int N, int d, int causal, float scale,
+             hipStream_t stream) {
     fa::BwdArgs a{};
-    int st = fill_bwd(a, q, k, v, dO, workspace, workspace_bytes, B, H, N, d, scale);
+    int st = fill_bwd(a, q, k, v, dO, workspace, workspace_bytes, B, H, Hkv, N, d, scale);
     if (st != FA_OK) return st;
     st = check_ptrs({dq});
     if (st != FA_OK) return st;
@@ -152,10 +164,26 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, con
     return fa::launch_bwd_dq(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-             int causal, float scale, hipStream_t stream) {
+}  // namespace
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                  size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                  hipStream_t stream) {
+    return dkdv_stage(q, k, v, dO, workspace, workspace_bytes, dk, dv, B, H, H, N, d, causal, scale, stream);
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal, float scale,
+                hipStream_t stream) {
+    return dq_stage(q, k, v, dO, workspace, workspace_bytes, dq, B, H, H, N, d, causal, scale, stream);
+}
+
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                 int d, int causal, float scale, hipStream_t stream) {
     int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    st = check_heads(H, Hkv);
     if (st != FA_OK) return st;
     st = check_ptrs({q, k, v, o, dO, lse, dq, dk, dv});
     if (st != FA_OK) return st;
@@ -163,9 +191,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (st != FA_OK) return st;
     st = attn_bwd_prep(o, dO, lse, workspace, workspace_bytes, B, H, N, d, stream);
     if (st != FA_OK) return st;
-    st = attn_bwd_dkdv(q, k, v, dO, workspace, workspace_bytes, dk, dv, B, H, N, d, causal, scale, stream);
+    st = dkdv_stage(q, k, v, dO, workspace, workspace_bytes, dk, dv, B, H, Hkv, N, d, causal, scale, stream);
     if (st != FA_OK) return st;
-    return attn_bwd_dq(q, k, v, dO, workspace, workspace_bytes, dq, B, H, N, d, causal, scale, stream);
+    return dq_stage(q, k, v, dO, workspace, workspace_bytes, dq, B, H, Hkv, N, d, causal, scale, stream);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+             int causal, float scale, hipStream_t stream) {
+    return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d, causal, scale,
+                        stream);
 }
 
 const char* fa_status_string(int status) {

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // accumulators each lane holds one key column (lane % 32) and 16 query rows,
 // which is exactly the B operand layout of dV^T += dO^T P and dK^T += Q^T dS,
 // whose A operands come from transposing reads of the same tiles.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool GQA>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     using T = LdsTile<D>;
     constexpr int NW = 4;
@@ -91,11 +91,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
     const int B = a.B, H = a.H, N = a.N;
     const int npad = (N + 63) & ~63;
+    const int Hkv = GQA ? a.Hkv : H;
+    const int G = GQA ? H / Hkv : 1;     // query heads sharing this K/V head
     const int nk = (N + BK - 1) / BK;
-    const int r = xcd_remap(blockIdx.x, nk * B * H);
-    const int bh = r / nk;
-    const int kb = r - bh * nk;          // causal: low key blocks see the most query tiles, so go first
-    const int b = bh / H, h = bh - b * H;
+    const int r = xcd_remap(blockIdx.x, nk * B * Hkv);
+    const int bhk = r / nk;
+    const int kb = r - bhk * nk;         // causal: low key blocks see the most query tiles, so go first
+    const int b = bhk / Hkv, hk = bhk - b * Hkv;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,14 +105,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    const size_t rs = (size_t)H * D;
-    const size_t base = ((size_t)b * N * H + h) * D;
-    const __bf16* Qg = static_cast<const __bf16*>(a.q) + base;
-    const __bf16* Kg = static_cast<const __bf16*>(a.k) + base;
-    const __bf16* Vg = static_cast<const __bf16*>(a.v) + base;
-    const __bf16* dOg = static_cast<const __bf16*>(a.dO) + base;
-    const float* ddg = a.dd + (size_t)bh * npad;
-    const float* lsg = a.lse2 + (size_t)bh * npad;
+    const size_t rs = (size_t)H * D;                  // Q / dO row stride
+    const size_t rskv = (size_t)Hkv * D;              // K / V / dK / dV row stride
+    const size_t kvbase = ((size_t)b * N * Hkv + hk) * D;
+    // Query head g of the group is h = hk * G + g: its Q / dO start D
+    // elements after head g - 1's, its statistics npad floats after.
+    const size_t qbase = ((size_t)b * N * H + (size_t)hk * G) * D;
+    const __bf16* Qg0 = static_cast<const __bf16*>(a.q) + qbase;
+    const __bf16* dOg0 = static_cast<const __bf16*>(a.dO) + qbase;
+    const __bf16* Kg = static_cast<const __bf16*>(a.k) + kvbase;
+    const __bf16* Vg = static_cast<const __bf16*>(a.v) + kvbase;
+    const size_t stat0 = ((size_t)b * H + (size_t)hk * G) * npad;
 
     const int k0 = kb * BK;
     const int kw = k0 + wave * 32;       // first key of this wave
@@ -122,8 +127,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     for (int c = 0; c < DC; ++c) {
         u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
         if (myk < N) {
-            kv = ld16(Kg + (size_t)myk * rs + c * 16 + hi * 8);
-            vv = ld16(Vg + (size_t)myk * rs + c * 16 + hi * 8);
+            kv = ld16(Kg + (size_t)myk * rskv + c * 16 + hi * 8);
+            vv = ld16(Vg + (size_t)myk * rskv + c * 16 + hi * 8);
         }
         kv ^= a.qsign;  // negative scale folded into S's operand
         kf[c] = as_bf16x8(kv);
@@ -147,16 +152,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     auto stage_ptr = [&](int s) { return smem + s * STAGE; };
     unsigned toff[T::NINST / NW];
     T::template offsets<NW>(toff, rs, wave, lane);
-    auto dma = [&](int t, int s) {
+    // Stage s receives query tile t of group head g.
+    auto dma = [&](int g, int t, int s) {
         unsigned char* st = stage_ptr(s);
         const int q0 = qstart + t * BQ;
-        T::template load<NW>(st, Qg, rs, q0, N, wave, lane, toff);
-        T::template load<NW>(st + T::BYTES, dOg, rs, q0, N, wave, lane, toff);
+        T::template load<NW>(st, Qg0 + (size_t)g * D, rs, q0, N, wave, lane, toff);
+        T::template load<NW>(st + T::BYTES, dOg0 + (size_t)g * D, rs, q0, N, wave, lane, toff);
         // q0 + 63 < npad: the padded statistics need no clamp.
+        const size_t so = stat0 + (size_t)g * npad + q0 + lane;
         if (wave == 0)
-            __builtin_amdgcn_global_load_lds(lsg + q0 + lane, (lds_void_t*)(st + 2 * T::BYTES), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(a.lse2 + so, (lds_void_t*)(st + 2 * T::BYTES), 4, 0, 0);
         if (wave == 1)
-            __builtin_amdgcn_global_load_lds(ddg + q0 + lane, (lds_void_t*)(st + 2 * T::BYTES + BQ * 4), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(a.dd + so, (lds_void_t*)(st + 2 * T::BYTES + BQ * 4), 4, 0, 0);
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
@@ -208,11 +215,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
     };
 
-    auto tile = [&](int t, auto masked_c) {
+    auto tile = [&](int s, int t, auto masked_c) {
         static_assert(MB == 2, "the schedule below is written for two 32-query blocks");
         constexpr bool masked = decltype(masked_c)::value;
         const int q0 = qstart + t * BQ;
-        const unsigned char* Qs = stage_ptr(t & 1);
+        const unsigned char* Qs = stage_ptr(s);
         const unsigned char* Gs = Qs + T::BYTES;
         const float* Ls = reinterpret_cast<const float*>(Qs + 2 * T::BYTES);
         const float* Ds = Ls + BQ;
@@ -291,27 +298,56 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     // Causal: only the first BK / BQ tiles (queries k0 .. k0+BK-1) straddle the
     // diagonal of this workgroup's keys; they run the masked variant, the
     // rest the variant without mask arithmetic.
+    // With grouped-query attention the G query heads of this K/V head are
+    // processed one after the other, all accumulating into the same dK, dV;
+    // the staged tiles run through them as one sequence n = g * ntiles + t.
     const int t_split = CAUSAL ? min(ntiles, BK / BQ) : 0;
-    dma(0, 0);
+    auto load_next = [&](int g, int t, int n) {
+        int gn = g, tn = t + 1;
+        if (tn == ntiles) {
+            gn = g + 1;
+            tn = 0;
+        }
+        if (gn < G) dma(gn, tn, (n + 1) & 1);
+    };
+    dma(0, 0, 0);
     wait_dma();
     __syncthreads();
-    for (int t = 0; t < t_split; ++t) {
-        if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
-        // Tiles whose last query precedes this wave's first key are empty.
-        if (qstart + t * BQ + BQ - 1 >= kw) tile(t, std::true_type{});
-        wait_dma();
-        __syncthreads();
-    }
-    for (int t = t_split; t < ntiles; ++t) {
-        if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
-        tile(t, std::false_type{});
-        wait_dma();
-        __syncthreads();
+    if constexpr (!GQA) {
+        for (int t = 0; t < t_split; ++t) {
+            if (t + 1 < ntiles) dma(0, t + 1, (t + 1) & 1);
+            // Tiles whose last query precedes this wave's first key are empty.
+            if (qstart + t * BQ + BQ - 1 >= kw) tile(t & 1, t, std::true_type{});
+            wait_dma();
+            __syncthreads();
+        }
+        for (int t = t_split; t < ntiles; ++t) {
+            if (t + 1 < ntiles) dma(0, t + 1, (t + 1) & 1);
+            tile(t & 1, t, std::false_type{});
+            wait_dma();
+            __syncthreads();
+        }
+    } else {
+        for (int g = 0; g < G; ++g) {
+            const int n0 = g * ntiles;
+            for (int t = 0; t < t_split; ++t) {
+                load_next(g, t, n0 + t);
+                if (qstart + t * BQ + BQ - 1 >= kw) tile((n0 + t) & 1, t, std::true_type{});
+                wait_dma();
+                __syncthreads();
+            }
+            for (int t = t_split; t < ntiles; ++t) {
+                load_next(g, t, n0 + t);
+                tile((n0 + t) & 1, t, std::false_type{});
+                wait_dma();
+                __syncthreads();
+            }
+        }
     }
 
     if (myk < N) {
-        __bf16* dkrow = static_cast<__bf16*>(a.dk) + base + (size_t)myk * rs;
-        __bf16* dvrow = static_cast<__bf16*>(a.dv) + base + (size_t)myk * rs;
+        __bf16* dkrow = static_cast<__bf16*>(a.dk) + kvbase + (size_t)myk * rskv;
+        __bf16* dvrow = static_cast<__bf16*>(a.dv) + kvbase + (size_t)myk * rskv;
         const float sc = a.scale;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -362,11 +398,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    const size_t rs = (size_t)H * D;
+    const size_t rs = (size_t)H * D;                  // Q / dO / dQ row stride
     const size_t base = ((size_t)b * N * H + h) * D;
+    const int hk = h / (H / a.Hkv);                   // K / V head of this query head
+    const size_t rskv = (size_t)a.Hkv * D;
+    const size_t kvbase = ((size_t)b * N * a.Hkv + hk) * D;
     const __bf16* Qg = static_cast<const __bf16*>(a.q) + base;
-    const __bf16* Kg = static_cast<const __bf16*>(a.k) + base;
-    const __bf16* Vg = static_cast<const __bf16*>(a.v) + base;
+    const __bf16* Kg = static_cast<const __bf16*>(a.k) + kvbase;
+    const __bf16* Vg = static_cast<const __bf16*>(a.v) + kvbase;
     const __bf16* dOg = static_cast<const __bf16*>(a.dO) + base;
 
     const int q0 = qb * BM;
@@ -402,10 +441,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     auto kbuf = [&](int s) { return smem + s * T::BYTES; };
     auto vbuf = [&](int s) { return smem + (2 + s) * T::BYTES; };
     unsigned toff[T::NINST / NW];
-    T::template offsets<NW>(toff, rs, wave, lane);
+    T::template offsets<NW>(toff, rskv, wave, lane);
     auto dma = [&](int t, int s) {
-        T::template load<NW>(kbuf(s), Kg, rs, t * BN, N, wave, lane, toff);
-        T::template load<NW>(vbuf(s), Vg, rs, t * BN, N, wave, lane, toff);
+        T::template load<NW>(kbuf(s), Kg, rskv, t * BN, N, wave, lane, toff);
+        T::template load<NW>(vbuf(s), Vg, rskv, t * BN, N, wave, lane, toff);
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
@@ -521,8 +560,11 @@ static hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
-    const long long g = (long long)((a.N + 127) / 128) * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g), dim3(256), 0, stream, a);
+    const long long g = (long long)((a.N + 127) / 128) * a.B * a.Hkv;
+    if (a.Hkv == a.H)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3((unsigned)g), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)g), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ struct FwdArgs {
     void* o;
     float* lse;
     int B, H, N;
+    int Hkv;          // K/V heads (H is a multiple; query head h reads K/V head h / (H / Hkv))
     float c2;         // |scale| * log2(e): scores are exponentiated in base 2
     uint32_t qsign;   // 0x80008000 when scale < 0 (folded into Q's sign bits), else 0
     float qsign_f;    // -1.0f when scale < 0, else 1.0f (fp32 kernels)
@@ -51,9 +52,10 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* dd;        // workspace: D_i = dO_i . O_i, fp32 [B, H, Npad]
+    float* dd;        // workspace: -D_i = -dO_i . O_i, fp32 [B, H, Npad]
     float* lse2;      // workspace: LSE_i * log2(e), fp32 [B, H, Npad] (+inf on padded rows)
     int B, H, N;
+    int Hkv;          // K/V heads, as in FwdArgs (k, v, dk, dv are [B, N, Hkv, d])
     float scale;      // the caller's scale (multiplies dQ and dK)
     float c2;         // |scale| * log2(e)
     uint32_t qsign;   // as in FwdArgs

@@ -89,11 +89,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    const size_t rs = (size_t)H * D;                       // row stride (elements)
+    const size_t rs = (size_t)H * D;                       // Q / O row stride (elements)
     const size_t base = ((size_t)b * N * H + h) * D;       // (b, 0, h, 0)
+    // K / V head of this query head (grouped-query attention when Hkv < H).
+    const int hk = h / (H / a.Hkv);
+    const size_t rskv = (size_t)a.Hkv * D;                 // K / V row stride
+    const size_t kvbase = ((size_t)b * N * a.Hkv + hk) * D;
     const __bf16* Qg = static_cast<const __bf16*>(a.q) + base;
-    const __bf16* Kg = static_cast<const __bf16*>(a.k) + base;
-    const __bf16* Vg = static_cast<const __bf16*>(a.v) + base;
+    const __bf16* Kg = static_cast<const __bf16*>(a.k) + kvbase;
+    const __bf16* Vg = static_cast<const __bf16*>(a.v) + kvbase;
     __bf16* Og = static_cast<__bf16*>(a.o) + base;
 
     const int q0 = qb * BM;
@@ -123,20 +127,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     // the tile; lane i writes LDS chunk slot i, so it fetches the global chunk
     // that the swizzle puts there. Rows past N are clamped to N-1 (they are
     // masked for K and meet P = 0 for V).
-    // Element offsets of this lane's chunks within a tile (row * rs + chunk)
-    // are fixed; a whole tile adds a uniform t * BN * rs. Only the ragged
+    // Element offsets of this lane's chunks within a tile (row * rskv +
+    // chunk) are fixed; a whole tile adds a uniform t * BN * rskv. Only the ragged
     // last tile recomputes them with the clamp.
     unsigned koff[IPW], voff[IPW];
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
         const int row = (wave + NW * j) * RPI + lane / CPR;
         const int slot = lane % CPR;
-        koff[j] = (unsigned)row * (unsigned)rs + 8u * (unsigned)(slot ^ swk(row));
-        voff[j] = (unsigned)row * (unsigned)rs + 8u * (unsigned)(slot ^ swv(row));
+        koff[j] = (unsigned)row * (unsigned)rskv + 8u * (unsigned)(slot ^ swk(row));
+        voff[j] = (unsigned)row * (unsigned)rskv + 8u * (unsigned)(slot ^ swv(row));
     }
     auto dma = [&](const __bf16* g, int t, int buf, bool is_v) {
         if ((t + 1) * BN <= N) {
-            const __bf16* gt = g + (size_t)t * BN * rs;
+            const __bf16* gt = g + (size_t)t * BN * rskv;
 #pragma unroll
             for (int j = 0; j < IPW; ++j) {
                 const int inst = wave + NW * j;
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
                 const int slot = lane % CPR;
                 const int c = slot ^ (is_v ? swv(row) : swk(row));
                 const int grow = min(t * BN + row, N - 1);
-                __builtin_amdgcn_global_load_lds(g + (size_t)grow * rs + c * 8,
+                __builtin_amdgcn_global_load_lds(g + (size_t)grow * rskv + c * 8,
                                                  (lds_void_t*)(smem + buf * TILE + inst * 1024), 16, 0, 0);
             }
         }

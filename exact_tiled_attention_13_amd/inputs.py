@@ -36,6 +36,11 @@ class Workload:
     causal: tuple       # masks the workload is run with
     backward: bool
     seed: int
+    Hkv: int = 0        # K/V heads for grouped-query attention (0: same as H)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -65,6 +70,10 @@ BWD_LONG = Workload("bwd_bf16_b1_h16_n16384_d128", "bf16", 1, 16, 16384, 128, (F
 # (H * d = 2048 as in every other workload); reported beside the main step.
 LONG_D64 = Workload("bwd_bf16_b1_h32_n16384_d64", "bf16", 1, 32, 16384, 64, (False, True), True, 1006)
 
+# Grouped-query attention at the long-context shape: 16 query heads sharing
+# 2 K/V heads (groups of 8); reported beside the main step.
+LONG_GQA = Workload("bwd_bf16_b1_h16_hkv2_n16384_d128", "bf16", 1, 16, 16384, 128, (False, True), True, 1007, Hkv=2)
+
 
 def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0, with_do: bool = False):
     """Draw Q, K, V (and dO) on the CPU. Returns a tuple of CPU tensors [B, N, H, d].
@@ -80,6 +89,20 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
     return tuple(out)
 
 
+def make_gqa(B: int, H: int, Hkv: int, N: int, d: int, dtype: str = "bf16", seed: int = 0, with_do: bool = False):
+    """Grouped-query inputs: Q [B, N, H, d], then K and V [B, N, Hkv, d] (and dO [B, N, H, d]), drawn in that
+    order from one generator, as make_qkv does."""
+    g = torch.Generator().manual_seed(seed)
+    heads = [H, Hkv, Hkv] + ([H] if with_do else [])
+    out = []
+    for h in heads:
+        t = torch.randn(B, N, h, d, dtype=torch.float32, generator=g)
+        out.append(t.to(torch.bfloat16) if dtype == "bf16" else t)
+    return tuple(out)
+
+
 def make_workload(w: Workload):
     """Inputs of a named workload: (q, k, v) or (q, k, v, do) on the CPU."""
+    if w.Hkv and w.Hkv != w.H:
+        return make_gqa(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, w.seed, with_do=w.backward)
     return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, with_do=w.backward)

@@ -67,7 +67,8 @@ extern "C" {
 /* Status codes returned by every int-valued entry point. */
 enum fa_status {
     FA_OK = 0,               /* work enqueued */
-    FA_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, size <= 0 or too large, non-finite scale */
+    FA_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, size <= 0 or too large, non-finite scale,
+                                H not a multiple of Hkv */
     FA_ERR_UNSUPPORTED = 2,  /* head dimension d not in {64, 128} */
     FA_ERR_WORKSPACE = 3,    /* workspace null or smaller than attn_bwd_workspace_size() */
     FA_ERR_HIP = 4           /* a HIP launch reported an error (hipGetLastError) */
@@ -121,6 +122,31 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes,
              int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Grouped-query and multi-query attention (page "FlashAttention-T:
+ * Optimización GPU para LLMs Escalables", section "Innovaciones técnicas
+ * frente a FlashAttention original", which lists both as natively supported):
+ * K and V have Hkv heads, H is a multiple of Hkv, and query head h attends
+ * with K/V head h / (H / Hkv) (Hkv = 1 is multi-query attention, Hkv = H is
+ * attn_fwd / attn_bwd).
+ *
+ * attn_fwd_gqa -- as attn_fwd, with k, v [B, N, Hkv, d] bf16; q, o
+ *   [B, N, H, d]; lse [B, H, N].
+ * attn_bwd_gqa -- as attn_bwd, with k, v, dk, dv [B, N, Hkv, d]: the gradient
+ *   of a K/V head is the sum over the H / Hkv query heads that read it
+ *   (accumulated in fp32 inside one workgroup, so the result is still
+ *   deterministic). The workspace is attn_bwd_workspace_size(B, H, N, d,
+ *   causal), sized by the query heads.
+ * Errors as for attn_fwd / attn_bwd, plus FA_ERR_INVALID_ARG when Hkv <= 0 or
+ * H is not a multiple of Hkv.
+ */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Hkv, int N, int d, int causal, float scale, hipStream_t stream);
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int H, int Hkv, int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
  * The three stages attn_bwd runs, in order, on one stream. They are exported

@@ -112,3 +112,20 @@ def test_backward_stages_reject_bad_arguments():
     assert L.attn_bwd_dq(P, P, P, P, P, need, 0, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
     assert L.attn_bwd_dq(P, P, P, P, 0, need, P, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_WORKSPACE
     assert L.attn_bwd_dq(P, P, P, P, P, need, P, 1, 0, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_gqa_rejects_bad_head_counts():
+    L = fa.lib()
+    # attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream)
+    assert L.attn_fwd_gqa(P, P, P, P, P, 1, 4, 3, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_fwd_gqa(P, P, P, P, P, 1, 4, 0, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_fwd_gqa(P, P, P, P, P, 1, 4, -2, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_fwd_gqa(P, P, P, P, P, 1, 4, 2, 16, 96, 0, 0.125, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.attn_fwd_gqa(P, P, 0, P, P, 1, 4, 2, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    need = fa.attn_bwd_workspace_size(1, 4, 16, 64, False)
+    # attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, ws, ws_bytes, B, H, Hkv, N, d, causal, scale, stream)
+    args = [P] * 10 + [need]
+    assert L.attn_bwd_gqa(*args, 1, 4, 3, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_gqa(*args, 1, 4, 0, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_gqa(*([P] * 10), need - 1, 1, 4, 2, 16, 64, 0, 0.125, None) == fa.FA_ERR_WORKSPACE
+    assert L.attn_bwd_gqa(*([P] * 6), 0, P, P, P, need, 1, 4, 2, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG

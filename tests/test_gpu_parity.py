@@ -189,3 +189,89 @@ def test_bwd_bf16_workload_n4096_sampled_heads():
     assert nerr(np.concatenate(got["o"]), np.concatenate(ref["o"])) <= TOL_O_BF16
     for name in ("dq", "dk", "dv"):
         assert nerr(np.concatenate(got[name]), np.concatenate(ref[name])) <= TOL_GRAD_BF16, name
+
+
+# ---------------------------------------------------------------------------
+# grouped-query / multi-query attention (K/V heads shared by query heads)
+
+def run_gqa(q, k, v, do, causal, scale):
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa.attn_fwd_gqa(qd, kd, vd, causal, scale)
+    dq, dk, dv = fa.attn_bwd_gqa(qd, kd, vd, o, dod, lse, causal, scale)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 1), (8, 2), (6, 3)])
+@pytest.mark.parametrize("N", [17, 257])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_bf16_shapes(H, Hkv, N, d, causal):
+    from oracle import attn_bwd_gqa, attn_fwd_gqa
+    g = torch.Generator().manual_seed(H * 100 + Hkv * 10 + N + d + causal)
+    q, do = (torch.randn(2, N, H, d, generator=g).to(torch.bfloat16) for _ in range(2))
+    k, v = (torch.randn(2, N, Hkv, d, generator=g).to(torch.bfloat16) for _ in range(2))
+    s = float(np.float32(d ** -0.5))
+    o, lse, dq, dk, dv = run_gqa(q, k, v, do, causal, s)
+    n = lambda t: t.double().numpy()
+    ro, rl = attn_fwd_gqa(n(q), n(k), n(v), causal, s)
+    rq, rk, rv = attn_bwd_gqa(n(q), n(k), n(v), n(do), causal, s)
+    assert nerr(f64(o), ro) <= TOL_O_BF16
+    assert aerr(f64(lse), rl) <= TOL_LSE_BF16
+    assert nerr(f64(dq), rq) <= TOL_GRAD_BF16
+    assert nerr(f64(dk), rk) <= TOL_GRAD_BF16
+    assert nerr(f64(dv), rv) <= TOL_GRAD_BF16
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_bf16_ragged_long_d128(causal):
+    """8-wave forward and dQ kernels (d = 128 beyond 2048 tokens), two K/V heads for four query heads."""
+    from oracle import attn_bwd_gqa, attn_fwd_gqa
+    N = 2113
+    g = torch.Generator().manual_seed(4242 + causal)
+    q, do = (torch.randn(1, N, 4, 128, generator=g).to(torch.bfloat16) for _ in range(2))
+    k, v = (torch.randn(1, N, 2, 128, generator=g).to(torch.bfloat16) for _ in range(2))
+    s = float(np.float32(128 ** -0.5))
+    o, lse, dq, dk, dv = run_gqa(q, k, v, do, causal, s)
+    n = lambda t: t.double().numpy()
+    ro, rl = attn_fwd_gqa(n(q), n(k), n(v), causal, s)
+    rq, rk, rv = attn_bwd_gqa(n(q), n(k), n(v), n(do), causal, s)
+    assert nerr(f64(o), ro) <= TOL_O_BF16
+    assert aerr(f64(lse), rl) <= TOL_LSE_BF16
+    assert nerr(f64(dq), rq) <= TOL_GRAD_BF16
+    assert nerr(f64(dk), rk) <= TOL_GRAD_BF16
+    assert nerr(f64(dv), rv) <= TOL_GRAD_BF16
+
+
+def test_gqa_with_hkv_equal_h_is_bitwise_mha():
+    q, k, v, do = make_qkv(1, 3, 300, 64, "bf16", seed=77, with_do=True)
+    s = float(np.float32(0.125))
+    a = run_gqa(q, k, v, do, True, s)
+    b = run_bwd(q, k, v, do, True, s)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_gqa_bf16_workload_n16384_sampled():
+    """The grouped-query workload the benchmark reports (16 query heads on 2 K/V
+    heads, 16k tokens, d 128), in the same launch configuration: sampled rows of
+    query heads in both groups against the oracle on their shared K/V head."""
+    from exact_tiled_attention_13_amd.inputs import LONG_GQA as w
+    q, k, v, _ = make_workload(w)
+    G = w.H // w.kv_heads
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for causal in w.causal:
+        o, lse = fa.attn_fwd_gqa(qd, kd, vd, causal, w.scale)
+        torch.cuda.synchronize()
+        o, lse = o.cpu(), lse.cpu()
+        got_o, ref_o, got_l, ref_l = [], [], [], []
+        for i, h in enumerate([0, 7, 8, 15]):
+            rows = sample_rows(w.N, 128, seed=w.seed + i)
+            ro, rl = attn_fwd_rows(q[0, :, h].double().numpy(), k[0, :, h // G].double().numpy(),
+                                   v[0, :, h // G].double().numpy(), rows, causal, w.scale)
+            got_o.append(f64(o[0, rows, h]))
+            ref_o.append(ro)
+            got_l.append(f64(lse[0, h, rows]))
+            ref_l.append(rl)
+        assert nerr(np.concatenate(got_o), np.concatenate(ref_o)) <= TOL_O_BF16, causal
+        assert aerr(np.concatenate(got_l), np.concatenate(ref_l)) <= TOL_LSE_BF16, causal
