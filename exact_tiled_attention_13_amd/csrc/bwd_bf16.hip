@@ -68,8 +68,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup of 4 waves per 128 keys (32 per wave, K and V rows in
-// VGPRs), looping over query tiles of 64 rows staged in LDS by direct loads.
+// dK, dV for d = 64: one workgroup of 4 waves per 128 keys (32 per wave, K
+// and V rows in VGPRs; two workgroups share a CU), looping over query tiles
+// of 64 rows staged in LDS by direct loads.
 //
 // S = Q K^T and dP = dO V^T use row reads of the Q / dO tiles; in their 32x32
 // accumulators each lane holds one key column (lane % 32) and 16 query rows,
@@ -366,6 +367,383 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV for d = 128: one workgroup of 8 waves per 128 keys, looping over
+// query tiles of 64 rows staged in LDS by direct loads. At d = 128 the four
+// products of a wave that owns 32 keys need more than 256 VGPRs (K, V, dK, dV
+// alone take 192), which would leave one wave per SIMD. Instead waves w and
+// w + 4 share the 32 keys k0 + 32 (w % 4) .. +31 and run on the same SIMD
+// with complementary work:
+//
+//   P wave  (w < 4):  S = Q K^T, P = exp2(S c2 - LSE2) (K rows in VGPRs),
+//                     dV^T += dO^T P; P goes to LDS in fp32 for the partner.
+//   dS wave (w >= 4): dP - D = dO V^T - D (V rows in VGPRs; the accumulator
+//                     starts at -D); one tile later, with the partner's P,
+//                     dS = P o (dP - D) and dK^T += Q^T dS.
+//
+// Either wave holds one set of key rows and one 32 x d accumulator, so two
+// waves fit a SIMD's registers, and while one wave is in its exponential or
+// product phase the other keeps the matrix core busy. The dS wave lags its
+// partner by one tile, so Q tiles are triple-buffered (the dS wave still
+// reads tile n - 1 while tile n + 1 loads) and everything else double-
+// buffered; one barrier per tile orders every LDS hand-over.
+//
+// In the 32x32 accumulators of S and dP each lane holds one key column
+// (lane % 32) and 16 query rows, which is exactly the B operand layout of
+// dV^T += dO^T P and dK^T += Q^T dS; their A operands come from transposing
+// reads of the dO and Q tiles.
+template <int D, bool CAUSAL, bool GQA>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
+    using T = LdsTile<D>;
+    constexpr int NW = 8;
+    constexpr int BK = 128;              // keys per workgroup
+    constexpr int BQ = T::ROWS;          // queries per tile
+    constexpr int DC = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int MB = BQ / 32;          // 32-query blocks per tile
+    constexpr int RB = T::RB;
+    static_assert(MB == 2, "the schedule below is written for two 32-query blocks");
+    constexpr int SST = 2 * BQ * 4;                    // statistics stage: LSE2[BQ], -D[BQ]
+    constexpr int PXG = MB * 4 * 1024;                 // P of one key group: per block, 4 rows of 1 KB
+    constexpr int PXB = 4 * PXG;                       // P exchange buffer (4 key groups)
+    constexpr int QOFF = 0;                            // Q tiles, 3 stages
+    constexpr int GOFF = 3 * T::BYTES;                 // dO tiles, 2 stages
+    constexpr int SOFF = 5 * T::BYTES;                 // statistics, 2 stages
+    constexpr int POFF = SOFF + 2 * SST;               // P exchange, 2 buffers
+    constexpr int LDS_BYTES = POFF + 2 * PXB;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+
+    const int B = a.B, H = a.H, N = a.N;
+    const int npad = (N + 63) & ~63;
+    const int Hkv = GQA ? a.Hkv : H;
+    const int G = GQA ? H / Hkv : 1;     // query heads sharing this K/V head
+    const int nk = (N + BK - 1) / BK;
+    const int r = xcd_remap(blockIdx.x, nk * B * Hkv);
+    const int bhk = r / nk;
+    const int kb = r - bhk * nk;         // causal: low key blocks see the most query tiles, so go first
+    const int b = bhk / Hkv, hk = bhk - b * Hkv;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    const int kg = wave & 3;             // key group
+    const bool pwave = wave < 4;
+
+    const size_t rs = (size_t)H * D;                  // Q / dO row stride
+    const size_t rskv = (size_t)Hkv * D;              // K / V / dK / dV row stride
+    const size_t kvbase = ((size_t)b * N * Hkv + hk) * D;
+    // Query head g of the group is h = hk * G + g: its Q / dO start D
+    // elements after head g - 1's, its statistics npad floats after.
+    const size_t qbase = ((size_t)b * N * H + (size_t)hk * G) * D;
+    const __bf16* Qg0 = static_cast<const __bf16*>(a.q) + qbase;
+    const __bf16* dOg0 = static_cast<const __bf16*>(a.dO) + qbase;
+    const size_t stat0 = ((size_t)b * H + (size_t)hk * G) * npad;
+
+    const int k0 = kb * BK;
+    const int kw = k0 + kg * 32;         // first key of this wave
+    const int myk = kw + l32;            // key column owned by this lane
+
+    // Key rows as B operands (lane holds row myk, d chunk c*16 + hi*8 .. +8):
+    // K for the P wave (negative scale folded into its sign), V for the dS wave.
+    bf16x8 rf[DC];
+    {
+        const __bf16* Rg = static_cast<const __bf16*>(pwave ? a.k : a.v) + kvbase;
+        const uint32_t sgn = pwave ? a.qsign : 0u;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (myk < N) x = ld16(Rg + (size_t)myk * rskv + c * 16 + hi * 8);
+            x ^= sgn;
+            rf[c] = as_bf16x8(x);
+        }
+    }
+
+    f32x16 acc[DB];                      // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+    const int qstart = CAUSAL ? k0 : 0;  // k0 is a multiple of BQ
+    const int ntiles = (N - qstart + BQ - 1) / BQ;
+    const float c2 = a.c2;
+    const int rowb = T::rowbase(lane);
+    const int trb0 = T::trbase(lane, 0);
+    const int trb1 = T::trbase(lane, 1);
+
+    auto qtile = [&](int s) { return smem + QOFF + s * T::BYTES; };
+    auto gtile = [&](int s) { return smem + GOFF + s * T::BYTES; };
+    auto stats = [&](int s) { return reinterpret_cast<float*>(smem + SOFF + s * SST); };
+    auto pxch = [&](int s) { return reinterpret_cast<float*>(smem + POFF + s * PXB + kg * PXG); };
+
+    // Only the P waves load tiles: a direct load stalls the issuing wave until
+    // the memory pipeline accepts it, and the P waves have slack at the
+    // barrier while the dS waves are the critical path.
+    constexpr int NL = 4;                // loading waves
+    unsigned toff[T::NINST / NL];
+    T::template offsets<NL>(toff, rs, kg, lane);
+    // Tile t of group head g: Q into Q stage qs, dO and statistics into stage gs.
+    auto dma = [&](int g, int t, int qs, int gs) {
+        if (!pwave) return;
+        const int q0 = qstart + t * BQ;
+        T::template load<NL>(qtile(qs), Qg0 + (size_t)g * D, rs, q0, N, kg, lane, toff);
+        T::template load<NL>(gtile(gs), dOg0 + (size_t)g * D, rs, q0, N, kg, lane, toff);
+        // q0 + 63 < npad: the padded statistics need no clamp.
+        const size_t so = stat0 + (size_t)g * npad + q0 + lane;
+        if (kg == 0) __builtin_amdgcn_global_load_lds(a.lse2 + so, (lds_void_t*)stats(gs), 4, 0, 0);
+        if (kg == 1) __builtin_amdgcn_global_load_lds(a.dd + so, (lds_void_t*)(stats(gs) + BQ), 4, 0, 0);
+    };
+    auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+
+    // Operand reads run PF MFMAs ahead of their use; sched_barrier(0) fences
+    // keep the compiler from regrouping the hand-placed stream.
+    constexpr int PF = 3;
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    constexpr int NJ = 2 * 2 * DB;       // MFMAs of the dV (or dK) phase
+    auto tr_off = [&](int j, int& o0, int& o1) {
+        const int mb = j / (2 * DB), db = (j / 2) % DB, half = j % 2;
+        const int qc = mb * 2 + half;
+        o0 = (trb0 ^ (db << 6)) + qc * 16 * RB;
+        o1 = (trb1 ^ (db << 6)) + qc * 16 * RB;
+    };
+    auto row_off = [&](int i) { return (rowb ^ ((i % DC) << 5)) + (i / DC) * 32 * RB; };
+
+    // ---- P wave: one tile -------------------------------------------------
+    // S = Q K^T (16 MFMAs), then dV^T += dO^T P (16 MFMAs). The softmax of
+    // block 0 runs in 8 parts under block 1's S MFMAs, block 1's under
+    // block 0's dV MFMAs. Part k computes elements 2k, 2k+1; odd parts also
+    // store the finished group of four to LDS and pack it to bf16.
+    auto p_tile = [&](int qs, int gs, int t, auto masked_c) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        const int q0 = qstart + t * BQ;
+        const unsigned char* Qs = qtile(qs);
+        const unsigned char* Gs = gtile(gs);
+        const float* Ls = stats(gs);
+        float* Px = pxch(gs);
+        // Causal diagonal: key myk is invisible to queries before it; thr is
+        // the key minus the element-0 query of the block.
+        const int thr[2] = {MASKED ? myk - (q0 + 4 * hi) : 0, MASKED ? myk - (q0 + 32 + 4 * hi) : 0};
+        f32x16 s[2];
+        f32x4 l4[2][4];
+        u32x4 pk[2][2];
+        auto soft = [&](int mb, int k) {
+#pragma unroll
+            for (int e = 2 * k; e < 2 * k + 2; ++e) {
+                float sv = s[mb][e];
+                if constexpr (MASKED) sv = (thr[mb] > 8 * (e >> 2) + (e & 3)) ? -INFINITY : sv;
+                s[mb][e] = exp2_fast(__builtin_fmaf(sv, c2, -l4[mb][e >> 2][e & 3]));
+            }
+            if (k & 1) {
+                const int g4 = k >> 1;
+                const f32x4 v = {s[mb][4 * g4], s[mb][4 * g4 + 1], s[mb][4 * g4 + 2], s[mb][4 * g4 + 3]};
+                *reinterpret_cast<f32x4*>(Px + (mb * 4 + g4) * 256 + lane * 4) = v;
+                pk[mb][g4 >> 1][2 * (g4 & 1)] = pack_bf16x2(v[0], v[1]);
+                pk[mb][g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16x2(v[2], v[3]);
+            }
+        };
+        bf16x8 ra[2 * DC];
+        auto row_load = [&](int i) { ra[i] = T::read_row(Qs, row_off(i)); };
+#pragma unroll
+        for (int i = 0; i < PF; ++i) row_load(i);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) l4[0][g4] = *reinterpret_cast<const f32x4*>(Ls + 8 * g4 + 4 * hi);
+        fence();
+#pragma unroll
+        for (int i = 0; i < 2 * DC; ++i) {
+            const int mb = i / DC;
+            if (i % DC == 0) s[mb] = f32x16{};
+            s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i], rf[i % DC], s[mb], 0, 0, 0);
+            if (i + PF < 2 * DC) row_load(i + PF);
+            if (i == DC - 1) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    l4[1][g4] = *reinterpret_cast<const f32x4*>(Ls + 32 + 8 * g4 + 4 * hi);
+            }
+            if (i >= DC) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (k * DC / 8 == i - DC) soft(0, k);
+            }
+            fence();
+        }
+        bf16x8 ta[NJ];
+        auto tr_load = [&](int j) {
+            int o0, o1;
+            tr_off(j, o0, o1);
+            ta[j] = T::read_tr(Gs, o0, o1);
+        };
+#pragma unroll
+        for (int j = 0; j < PF; ++j) tr_load(j);
+        fence();
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int mb = j / (2 * DB), db = (j / 2) % DB, half = j % 2;
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j], as_bf16x8(pk[mb][half]), acc[db], 0, 0, 0);
+            if (j + PF < NJ) tr_load(j + PF);
+            if (mb == 0) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (k * (2 * DB) / 8 == j) soft(1, k);
+            }
+            fence();
+        }
+    };
+
+    // ---- dS wave: one step -------------------------------------------------
+    // prev: finish the previous tile (its P in exchange buffer pgs, its Q in
+    // stage qsp): dS = P o (dP - D), then dK^T += Q^T dS (16 MFMAs).
+    // cur: dP - D of the current tile (dO stage gs; 16 MFMAs), kept in dp for
+    // the next step. Block 0's dS is done before block 0's accumulator is
+    // re-seeded; block 1's runs under block 0's dP MFMAs.
+    f32x16 dp[2];
+    auto ds_step = [&](int gs, int qsp, int pgs, bool prev, bool cur) {
+        const unsigned char* Gs = gtile(gs);
+        const float* Ds = stats(gs) + BQ;
+        const unsigned char* Qp = qtile(qsp);
+        const float* Pp = pxch(pgs);
+        f32x4 pr[2][4];
+        u32x4 sk[2][2];
+        auto ds_part = [&](int mb, int k) {
+            float v[2];
+#pragma unroll
+            for (int e = 2 * k; e < 2 * k + 2; ++e) v[e - 2 * k] = pr[mb][e >> 2][e & 3] * dp[mb][e];
+            // (elements 2k, 2k+1 form one packed word)
+            sk[mb][k >> 2][k & 3] = pack_bf16x2(v[0], v[1]);
+        };
+        bf16x8 rb[2 * DC];
+        auto row_load = [&](int i) { rb[i] = T::read_row(Gs, row_off(i)); };
+        if (prev) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    pr[mb][g4] = *reinterpret_cast<const f32x4*>(Pp + (mb * 4 + g4) * 256 + lane * 4);
+        }
+        if (cur) {
+#pragma unroll
+            for (int i = 0; i < PF; ++i) row_load(i);
+        }
+        fence();
+        if (prev) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) ds_part(0, k);
+        }
+        fence();
+        if (cur) {
+#pragma unroll
+            for (int i = 0; i < 2 * DC; ++i) {
+                const int mb = i / DC;
+                if (i % DC == 0) {
+                    // The accumulator starts at -D of its 16 query rows
+                    // (element u is query 8*(u/4) + 4*hi + u%4 of the block).
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + mb * 32 + 8 * g4 + 4 * hi);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) dp[mb][4 * g4 + e] = d4[e];
+                    }
+                }
+                dp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[i], rf[i % DC], dp[mb], 0, 0, 0);
+                if (i + PF < 2 * DC) row_load(i + PF);
+                if (prev && i < DC) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (k * DC / 8 == i) ds_part(1, k);
+                }
+                fence();
+            }
+        } else if (prev) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) ds_part(1, k);
+        }
+        if (prev) {
+            bf16x8 tb[NJ];
+            auto tr_load = [&](int j) {
+                int o0, o1;
+                tr_off(j, o0, o1);
+                tb[j] = T::read_tr(Qp, o0, o1);
+            };
+#pragma unroll
+            for (int j = 0; j < PF; ++j) tr_load(j);
+            fence();
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int mb = j / (2 * DB), db = (j / 2) % DB, half = j % 2;
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[j], as_bf16x8(sk[mb][half]), acc[db], 0, 0, 0);
+                if (j + PF < NJ) tr_load(j + PF);
+                fence();
+            }
+        }
+    };
+
+    // Tiles run as one sequence n over (group head g, tile t). Causal: only
+    // the first BK / BQ tiles of a head (queries k0 .. k0+BK-1) straddle the
+    // diagonal; they run the masked variant. A tile whose last query precedes
+    // a wave's first key is empty for that key group and skipped by both of
+    // its waves. Both roles pass the same barriers, one per tile.
+    const int t_split = CAUSAL ? min(ntiles, BK / BQ) : 0;
+    auto nonempty = [&](int t) { return !CAUSAL || qstart + t * BQ + BQ - 1 >= kw; };
+    auto dma_next = [&](int g, int t, int qs, int gs) {
+        int gn = g, tn = t + 1;
+        if (tn == ntiles) {
+            gn = g + 1;
+            tn = 0;
+        }
+        if (gn < G) dma(gn, tn, qs == 2 ? 0 : qs + 1, gs ^ 1);
+    };
+    dma(0, 0, 0, 0);
+    wait_dma();
+    __syncthreads();
+    int qs = 0, n = 0;
+    if (pwave) {
+        auto step = [&](int g, int t, auto masked_c) {
+            const int gs = n & 1;
+            dma_next(g, t, qs, gs);
+            if (nonempty(t)) p_tile(qs, gs, t, masked_c);
+            wait_dma();
+            __syncthreads();
+            qs = qs == 2 ? 0 : qs + 1;
+            ++n;
+        };
+        for (int g = 0; g < G; ++g) {
+            for (int t = 0; t < t_split; ++t) step(g, t, std::true_type{});
+            for (int t = t_split; t < ntiles; ++t) step(g, t, std::false_type{});
+        }
+    } else {
+        bool prev = false;
+        for (int g = 0; g < G; ++g) {
+            for (int t = 0; t < ntiles; ++t) {
+                const int gs = n & 1;
+                dma_next(g, t, qs, gs);
+                const bool cur = nonempty(t);
+                ds_step(gs, qs == 0 ? 2 : qs - 1, gs ^ 1, prev, cur);
+                prev = cur;
+                wait_dma();
+                __syncthreads();
+                qs = qs == 2 ? 0 : qs + 1;
+                ++n;
+            }
+        }
+        ds_step(0, qs == 0 ? 2 : qs - 1, (n - 1) & 1, prev, false);
+    }
+
+    if (myk < N) {
+        __bf16* row = static_cast<__bf16*>(pwave ? a.dv : a.dk) + kvbase + (size_t)myk * rskv;
+        const float sc = pwave ? 1.0f : a.scale;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + 8 * g + 4 * hi;
+                u32x2 w;
+                w[0] = pack_bf16x2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc);
+                w[1] = pack_bf16x2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
+                st8(row + d0, w);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: one workgroup of NW = 8 or 4 waves (two per SIMD) per 32*NW queries
 // (32 per wave, Q and dO rows in VGPRs), looping over key tiles of 64 rows
 // staged in LDS by direct loads, double-buffered. S^T = K Q^T and dP^T = V dO^T use row reads of the K and V
@@ -561,10 +939,19 @@ static hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
     const long long g = (long long)((a.N + 127) / 128) * a.B * a.Hkv;
-    if (a.Hkv == a.H)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3((unsigned)g), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)g), dim3(256), 0, stream, a);
+    // d = 128: the 8-wave P / dS pair kernel (7-8% faster at 16k tokens).
+    // d = 64: the 4-wave kernel, which already fits two workgroups per CU.
+    if constexpr (D == 128) {
+        if (a.Hkv == a.H)
+            hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL, false>), dim3((unsigned)g), dim3(512), 0, stream, a);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL, true>), dim3((unsigned)g), dim3(512), 0, stream, a);
+    } else {
+        if (a.Hkv == a.H)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3((unsigned)g), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)g), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
