@@ -32,6 +32,13 @@ Modules:
   LLMs Escalables", section "Innovaciones técnicas frente a FlashAttention
   original"), defined head by head through :mod:`oracle.attn_ref`.
 
+* :mod:`oracle.decode` -- decoding: a few new query rows against a key/value
+  cache (bottom-right causal alignment), the attention restricted to a key
+  chunk, and the exact merge of per-chunk (O, LSE) results (split-KV); page
+  "FlashAttention-2: atención eficiente en GPU para contextos largos",
+  section "Cómo documentar una diferencia técnica", which separates prefill
+  from decoding.
+
 Every function is pinned by ``tests/test_oracle*.py`` (brute force, torch CPU
 fp64 library routines, closed forms, invariants, finite differences and the
 hand-derived fixtures in ``tests/golden/``). No function here is "parity
@@ -48,3 +55,4 @@ from .attn_ref import (  # noqa: F401
     flops_bwd,
 )
 from .gqa import attn_bwd_gqa, attn_fwd_gqa  # noqa: F401
+from .decode import attn_decode, attn_decode_split, attn_partial, bytes_decode, merge_partials  # noqa: F401
