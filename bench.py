@@ -140,6 +140,40 @@ def time_passes(w, reps=10, warmup=3):
     return out
 
 
+def decode_bytes(B, H, Hkv, Nq, Nk, d):
+    """Compulsory HBM bytes of one bf16 decode call: K and V of the cache, Q, O (bf16) and LSE (fp32)."""
+    return 2.0 * 2 * B * Nk * Hkv * d + 2.0 * 2 * B * Nq * H * d + 4.0 * B * H * Nq
+
+
+def time_decode(w, reps=20, warmup=5):
+    """Report-only timing of a decoding workload (attn_decode: split kernel and merge), HIP events around
+    `reps` back-to-back calls; the rate is compulsory bytes over time against the 8 TB/s HBM peak."""
+    import torch
+
+    import exact_tiled_attention_13_amd as fa
+    from exact_tiled_attention_13_amd.inputs import make_decode
+
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in make_decode(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed))
+    ws = torch.empty(fa.attn_decode_workspace_size(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d), dtype=torch.uint8, device=dev)
+    out = {}
+    for c in w.causal:
+        o, lse = fa.attn_decode(q, k, v, c, w.scale, ws=ws)
+        for _ in range(warmup):
+            fa.attn_decode(q, k, v, c, w.scale, o=o, lse=lse, ws=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fa.attn_decode(q, k, v, c, w.scale, o=o, lse=lse, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = decode_bytes(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d) / ms / 1e6
+        out["decode_" + ("causal" if c else "noncausal")] = {
+            "ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,13 +319,18 @@ def main():
     }
     # Report-only: the other 16k-token workloads (head dim 64 at 16k tokens,
     # grouped-query attention at 16k tokens, the short-sequence and mid-length
-    # configurations, the batched backward).
+    # configurations, the batched backward) and decoding against a 16k-token
+    # cache (HBM-bound: reported in GB/s).
     from exact_tiled_attention_13_amd.inputs import LONG_D64, LONG_GQA, WORKLOADS
 
     if not args.no_report:
         report = {LONG_D64.name: time_passes(LONG_D64), LONG_GQA.name: time_passes(LONG_GQA)}
         for name in ("fwd_bf16_b32_h32_n512_d64", "fwd_bf16_b8_h16_n2048_d128", "bwd_bf16_b4_h16_n4096_d128"):
             report[name] = time_passes(WORKLOADS[name])
+        from exact_tiled_attention_13_amd.inputs import DECODE_1, DECODE_4
+
+        for dw in (DECODE_1, DECODE_4):
+            report[dw.name] = time_decode(dw)
         out["other_workloads"] = report
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale)

@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     attn_bwd_gqa,
     attn_bwd_prep,
     attn_bwd_workspace_size,
+    attn_decode,
+    attn_decode_workspace_size,
     attn_fwd,
     attn_fwd_fp32,
     attn_fwd_gqa,

@@ -24,7 +24,8 @@ FA_ERR_WORKSPACE = 3
 FA_ERR_HIP = 4
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_prep",
-            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_gqa", "attn_bwd_gqa", "fa_status_string")
+            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_gqa", "attn_bwd_gqa", "attn_decode_workspace_size",
+            "attn_decode", "fa_status_string")
 
 _lock = threading.Lock()
 _lib = None
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
             L.attn_fwd_gqa.restype = ci
             L.attn_bwd_gqa.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, ci, cf, vp]
             L.attn_bwd_gqa.restype = ci
+            L.attn_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+            L.attn_decode_workspace_size.restype = sz
+            L.attn_decode.argtypes = [vp] * 5 + [vp, sz] + [ci, ci, ci, ci, ci, ci, ci, cf, vp]
+            L.attn_decode.restype = ci
             L.fa_status_string.argtypes = [ci]
             L.fa_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -271,3 +276,35 @@ def attn_bwd_gqa(q, k, v, o, do, lse, causal: bool = False, scale: float | None 
                                               _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace), B, H, Hkv,
                                               N, d, int(bool(causal)), s, _stream(dev)))
     return dq, dk, dv
+
+
+def attn_decode_workspace_size(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    """Bytes of scratch attn_decode needs for this shape (0 if the library rejects the shape)."""
+    return int(lib().attn_decode_workspace_size(B, H, Hkv, Nq, Nk, d))
+
+
+def attn_decode(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None, ws=None):
+    """Decoding against a cache: q [B, Nq, H, d], k, v [B, Nk, Hkv, d] bf16. Returns (o, lse).
+
+    Query i is the token at position Nk - Nq + i (causal: it sees keys <= that
+    position). ``ws`` is an optional uint8 workspace of at least
+    attn_decode_workspace_size(...) bytes; one is allocated when omitted.
+    """
+    B, Nq, H, d = _shape(q)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k: expected [B, Nk, Hkv, d] = [{B}, Nk, Hkv, {d}], got {tuple(k.shape)}")
+    Nk, Hkv = int(k.shape[1]), int(k.shape[2])
+    dev = q.device
+    _expect("q", q, (B, Nq, H, d), torch.bfloat16, dev)
+    for name, t in (("k", k), ("v", v)):
+        _expect(name, t, (B, Nk, Hkv, d), torch.bfloat16, dev)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev) if lse is None else lse
+    _expect("o", o, (B, Nq, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, Nq), torch.float32, dev)
+    if ws is None:
+        ws = torch.empty(max(attn_decode_workspace_size(B, H, Hkv, Nq, Nk, d), 256), dtype=torch.uint8, device=dev)
+    s = default_scale(d) if scale is None else float(scale)
+    _check("attn_decode", lib().attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), _nbytes(ws),
+                                            B, H, Hkv, Nq, Nk, d, int(bool(causal)), s, _stream(dev)))
+    return o, lse

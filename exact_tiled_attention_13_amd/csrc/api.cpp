@@ -118,6 +118,8 @@ int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspa
     return fa::launch_bwd_prep(a, d, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+}  // extern "C"
+
 namespace {
 
 int fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* dO, const void* workspace,
@@ -166,6 +168,8 @@ int dq_stage(const void* q, const void* k, const void* v, const void* dO, const 
 
 }  // namespace
 
+extern "C" {
+
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
                   size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
                   hipStream_t stream) {
@@ -201,6 +205,66 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int causal, float scale, hipStream_t stream) {
     return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d, causal, scale,
                         stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Decode shape checks and workspace layout: per-chunk outputs fp32
+// [B, Hkv, S, R, d], then per-chunk LSE fp32 [B, Hkv, S, R].
+int check_decode(int B, int H, int Hkv, int Nq, int Nk, int d, float scale) {
+    if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)Nk * Hkv * d >= (1LL << 31) || (long long)Nq * H * d >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    if ((long long)B * Nk * Hkv * d >= (1LL << 40)) return FA_ERR_INVALID_ARG;
+    if ((long long)(H / Hkv) * Nq > 32) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+size_t decode_part_elems(int B, int H, int Hkv, int Nq, int Nk, int d) {
+    int L;
+    const int S = fa::decode_chunks(B, Hkv, Nk, &L);
+    return (size_t)B * Hkv * S * (size_t)((H / Hkv) * Nq) * d;
+}
+
+size_t decode_ws_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
+    const size_t o = decode_part_elems(B, H, Hkv, Nq, Nk, d);
+    const size_t raw = (o + o / d) * sizeof(float);
+    return (raw + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
+    if (check_decode(B, H, Hkv, Nq, Nk, d, 1.0f) != FA_OK) return 0;
+    return decode_ws_bytes(B, H, Hkv, Nq, Nk, d);
+}
+
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                hipStream_t stream) {
+    int st = check_decode(B, H, Hkv, Nq, Nk, d, scale);
+    if (st != FA_OK) return st;
+    if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
+    st = check_ptrs({q, k, v, o, lse});
+    if (st != FA_OK) return st;
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < decode_ws_bytes(B, H, Hkv, Nq, Nk, d))
+        return FA_ERR_WORKSPACE;
+    fa::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk;
+    a.R = (H / Hkv) * Nq;
+    a.S = fa::decode_chunks(B, Hkv, Nk, &a.L);
+    a.opart = static_cast<float*>(workspace);
+    a.lpart = a.opart + decode_part_elems(B, H, Hkv, Nq, Nk, d);
+    float unused;
+    fill_scale(scale, a.c2, a.qsign, unused);
+    return fa::launch_decode(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_status_string(int status) {

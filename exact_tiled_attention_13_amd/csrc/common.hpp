@@ -61,6 +61,25 @@ struct BwdArgs {
     uint32_t qsign;   // as in FwdArgs
 };
 
+// Launch arguments of the decoding kernels. q, o are [B, Nq, H, d]; k, v the
+// cache [B, Nk, Hkv, d]; lse [B, H, Nq]. Query row r (0 <= r < R) of K/V head
+// hk is query i = r / G of head hk * G + r % G, G = H / Hkv.
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    float* opart;     // workspace: per-chunk outputs, fp32 [B, Hkv, S, R, d]
+    float* lpart;     // workspace: per-chunk LSE (natural log), fp32 [B, Hkv, S, R]
+    int B, H, Hkv, Nq, Nk;
+    int R;            // query rows per K/V head, G * Nq (at most 32)
+    int S;            // key chunks
+    int L;            // keys per chunk (a multiple of 32); chunk s is keys s*L .. min((s+1)*L, Nk)-1
+    float c2;         // as in FwdArgs
+    uint32_t qsign;   // as in FwdArgs
+};
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Remap the dispatch index so that XCD x receives a contiguous range of
 // logical tile indices: the query blocks of one head then run on one XCD at

@@ -1,6 +1,6 @@
 // lds_tile.hpp -- LDS staging of 64-row bf16 tiles for the backward kernels.
 //
-// A tile is 64 rows of one head's [*, d] slice (row stride H*d elements in
+// A tile is ROWS (64 unless stated) rows of one head's [*, d] slice (row stride H*d elements in
 // global memory), stored in LDS unpadded, RB = 2d bytes per row, with the
 // 16-byte chunks of each row permuted by an XOR swizzle f(row). The swizzle is
 // chosen so that both access patterns the MFMA operands need are free of LDS
@@ -19,9 +19,10 @@ namespace fa {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
-template <int D>
+template <int D, int ROWS_ = 64>
 struct LdsTile {
-    static constexpr int ROWS = 64;
+    static_assert(ROWS_ % 16 == 0, "tiles are whole 16-row swizzle groups");
+    static constexpr int ROWS = ROWS_;
     static constexpr int RB = D * 2;            // bytes per row
     static constexpr int BYTES = ROWS * RB;     // bytes per tile
     static constexpr int NINST = BYTES / 1024;  // direct-to-LDS wave loads per tile

@@ -75,6 +75,44 @@ LONG_D64 = Workload("bwd_bf16_b1_h32_n16384_d64", "bf16", 1, 32, 16384, 64, (Fal
 LONG_GQA = Workload("bwd_bf16_b1_h16_hkv2_n16384_d128", "bf16", 1, 16, 16384, 128, (False, True), True, 1007, Hkv=2)
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Decoding: Nq new query rows per sequence against a cache of Nk keys and values."""
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: tuple
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+
+# Token-by-token generation against a 16k-token cache (the longest context of
+# the sweep above): 16 sequences, 32 query heads in groups of 4 per K/V head,
+# one new token each (the causal mask then hides nothing); and 4 new tokens
+# at once under the causal mask. The pages describe no decoding workload;
+# these are the plainest shapes that keep the cache at 16k tokens and H * d at
+# 4096 query features.
+DECODE_1 = DecodeWorkload("decode_bf16_b16_h32_hkv8_nq1_nk16384_d128", 16, 32, 8, 1, 16384, 128, (False,), 1008)
+DECODE_4 = DecodeWorkload("decode_bf16_b16_h32_hkv8_nq4_nk16384_d128", 16, 32, 8, 4, 16384, 128, (True,), 1009)
+
+
+def make_decode(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int = 0):
+    """Decoding inputs on the CPU: Q [B, Nq, H, d], then K and V [B, Nk, Hkv, d], drawn in that order
+    from one generator (randn, float32, rounded to bfloat16)."""
+    g = torch.Generator().manual_seed(seed)
+    out = []
+    for n, h in ((Nq, H), (Nk, Hkv), (Nk, Hkv)):
+        out.append(torch.randn(B, n, h, d, dtype=torch.float32, generator=g).to(torch.bfloat16))
+    return tuple(out)
+
+
 def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0, with_do: bool = False):
     """Draw Q, K, V (and dO) on the CPU. Returns a tuple of CPU tensors [B, N, H, d].
 

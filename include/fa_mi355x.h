@@ -173,6 +173,43 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, con
                 size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal, float scale,
                 hipStream_t stream);
 
+/*
+ * Decoding against a key/value cache (page "FlashAttention-2: atención
+ * eficiente en GPU para contextos largos", section "Cómo documentar una
+ * diferencia técnica", which separates the first pass over a context from
+ * token-by-token generation). The same exact attention as attn_fwd_gqa for
+ * Nq new query rows against Nk cached keys; query i is the token at position
+ * Nk - Nq + i, so with causal != 0 it sees keys j <= Nk - Nq + i (the mask is
+ * aligned to the last key; with Nq = Nk it is attn_fwd_gqa's).
+ *
+ * attn_decode_workspace_size -- bytes of scratch attn_decode needs for this
+ *   shape (per-chunk partial outputs and LSE, fp32); 0 if the shape is
+ *   rejected.
+ * attn_decode -- bf16 decoding, split over the key range:
+ *   q        [B, Nq, H, d] bf16, device, read-only.
+ *   k, v     the cache, [B, Nk, Hkv, d] bf16 (d fastest), device, read-only.
+ *   o        output [B, Nq, H, d] bf16, fully overwritten.
+ *   lse      output [B, H, Nq] fp32, natural-log log-sum-exp of each row.
+ *   workspace, workspace_bytes: caller-owned device scratch of at least
+ *            attn_decode_workspace_size(...) bytes, 256-byte aligned; its
+ *            contents on entry are ignored and on return are unspecified.
+ *   B, H, Hkv, Nq, Nk, d: H a multiple of Hkv; d in {64, 128}.
+ * Each chunk of keys gives every query row the attention restricted to it,
+ *     O_s (normalised within the chunk) and LSE_s,
+ * and the rows are combined exactly:
+ *     LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s.
+ * Errors: FA_ERR_INVALID_ARG for a null or unaligned pointer, B, H, Hkv, Nq
+ * or Nk < 1, H not a multiple of Hkv, causal with Nq > Nk, a non-finite scale
+ * or sizes past the limits of attn_fwd; FA_ERR_UNSUPPORTED for d not in
+ * {64, 128} or more than 32 query rows per K/V head ((H / Hkv) * Nq > 32);
+ * FA_ERR_WORKSPACE for a null, unaligned or too small workspace;
+ * FA_ERR_HIP when a launch fails. Asynchronous on `stream`.
+ */
+size_t attn_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d);
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                void* workspace, size_t workspace_bytes,
+                int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, hipStream_t stream);
+
 /* fa_status_string -- static, human-readable name of a status code. Never NULL. */
 const char* fa_status_string(int status);
 

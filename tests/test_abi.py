@@ -129,3 +129,36 @@ def test_gqa_rejects_bad_head_counts():
     assert L.attn_bwd_gqa(*args, 1, 4, 0, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
     assert L.attn_bwd_gqa(*([P] * 10), need - 1, 1, 4, 2, 16, 64, 0, 0.125, None) == fa.FA_ERR_WORKSPACE
     assert L.attn_bwd_gqa(*([P] * 6), 0, P, P, P, need, 1, 4, 2, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+
+
+def dec(q=P, k=P, v=P, o=P, lse=P, ws=P, wsb=1 << 30, B=1, H=8, Hkv=2, Nq=1, Nk=100, d=128, causal=0, scale=0.1):
+    return fa.lib().attn_decode(q, k, v, o, lse, ws, wsb, B, H, Hkv, Nq, Nk, d, causal, scale, None)
+
+
+def test_decode_workspace_size():
+    L = fa.lib()
+    n = L.attn_decode_workspace_size(2, 8, 2, 3, 1000, 128)
+    assert n > 0 and n % 256 == 0
+    # At least the per-chunk outputs and LSE of every query row of the workgroups that cover the cache.
+    assert n >= 2 * 2 * (4 * 3) * (128 + 1) * 4
+    assert L.attn_decode_workspace_size(1, 8, 3, 1, 10, 128) == 0      # H not a multiple of Hkv
+    assert L.attn_decode_workspace_size(1, 64, 1, 1, 10, 128) == 0     # 64 query rows per K/V head
+    assert L.attn_decode_workspace_size(1, 8, 2, 1, 10, 96) == 0       # head dim
+    assert L.attn_decode_workspace_size(1, 8, 2, 0, 10, 128) == 0
+
+
+def test_decode_rejects_bad_arguments():
+    assert dec(q=0) == fa.FA_ERR_INVALID_ARG
+    assert dec(lse=MIS) == fa.FA_ERR_INVALID_ARG
+    assert dec(B=0) == fa.FA_ERR_INVALID_ARG
+    assert dec(Nq=0) == fa.FA_ERR_INVALID_ARG
+    assert dec(Nk=0) == fa.FA_ERR_INVALID_ARG
+    assert dec(Hkv=3) == fa.FA_ERR_INVALID_ARG
+    assert dec(Hkv=0) == fa.FA_ERR_INVALID_ARG
+    assert dec(scale=float("inf")) == fa.FA_ERR_INVALID_ARG
+    assert dec(causal=1, Nq=8, Nk=4, H=2, Hkv=2) == fa.FA_ERR_INVALID_ARG   # more new tokens than cached keys
+    assert dec(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert dec(H=32, Hkv=1, Nq=2) == fa.FA_ERR_UNSUPPORTED                 # 64 query rows per K/V head
+    assert dec(ws=0) == fa.FA_ERR_WORKSPACE
+    assert dec(ws=MIS) == fa.FA_ERR_WORKSPACE
+    assert dec(wsb=16) == fa.FA_ERR_WORKSPACE
