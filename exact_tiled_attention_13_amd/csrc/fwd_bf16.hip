@@ -130,21 +130,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     // Element offsets of this lane's chunks within a tile (row * rskv +
     // chunk) are fixed; a whole tile adds a uniform t * BN * rskv. Only the ragged
     // last tile recomputes them with the clamp.
-    unsigned koff[IPW], voff[IPW];
-#pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-        const int row = (wave + NW * j) * RPI + lane / CPR;
+    // The swizzle bits of a row depend only on the row's position within its
+    // group of 16 (d = 128) or 8 row pairs (d = 64), and wave load j + 1
+    // covers the rows of load j shifted by NW * RPI (a multiple of that
+    // group), so one per-lane offset per tensor serves every load of the
+    // tile; load j adds the uniform j * NW * RPI rows.
+    static_assert((NW * RPI) % 16 == 0, "wave loads must keep the row swizzle");
+    unsigned koff0, voff0;
+    {
+        const int row = wave * RPI + lane / CPR;
         const int slot = lane % CPR;
-        koff[j] = (unsigned)row * (unsigned)rskv + 8u * (unsigned)(slot ^ swk(row));
-        voff[j] = (unsigned)row * (unsigned)rskv + 8u * (unsigned)(slot ^ swv(row));
+        koff0 = (unsigned)row * (unsigned)rskv + 8u * (unsigned)(slot ^ swk(row));
+        voff0 = (unsigned)row * (unsigned)rskv + 8u * (unsigned)(slot ^ swv(row));
     }
+    const size_t jstep = (size_t)NW * RPI * rskv;   // elements between load j and j + 1
     auto dma = [&](const __bf16* g, int t, int buf, bool is_v) {
         if ((t + 1) * BN <= N) {
             const __bf16* gt = g + (size_t)t * BN * rskv;
 #pragma unroll
             for (int j = 0; j < IPW; ++j) {
                 const int inst = wave + NW * j;
-                __builtin_amdgcn_global_load_lds(gt + (size_t)(is_v ? voff[j] : koff[j]),
+                __builtin_amdgcn_global_load_lds(gt + j * jstep + (size_t)(is_v ? voff0 : koff0),
                                                  (lds_void_t*)(smem + buf * TILE + inst * 1024), 16, 0, 0);
             }
         } else {
