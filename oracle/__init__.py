@@ -39,6 +39,10 @@ Modules:
   section "Cómo documentar una diferencia técnica", which separates prefill
   from decoding.
 
+* :mod:`oracle.fp8` -- the FP8 (E4M3) forward: the E4M3 rounding and the
+  tiled online softmax with 8-bit probabilities (page "FlashAttention-T:
+  Optimización GPU para LLMs Escalables", which names FP8 support only).
+
 Every function is pinned by ``tests/test_oracle*.py`` (brute force, torch CPU
 fp64 library routines, closed forms, invariants, finite differences and the
 hand-derived fixtures in ``tests/golden/``). No function here is "parity
@@ -56,3 +60,4 @@ from .attn_ref import (  # noqa: F401
 )
 from .gqa import attn_bwd_gqa, attn_fwd_gqa  # noqa: F401
 from .decode import attn_decode, attn_decode_split, attn_partial, bytes_decode, merge_partials  # noqa: F401
+from .fp8 import attn_fwd_fp8, quantize_e4m3, round_e4m3  # noqa: F401

@@ -1,0 +1,107 @@
+"""Pins of the FP8 oracle (oracle.fp8) against things other than itself:
+
+* the E4M3 code table and the rounding of random and hand-picked values
+  (ties, subnormals, saturation) against torch's float8_e4m3fn conversion
+  (independent library code);
+* a hand-derived fixture (tests/golden/hand_fp8_n2_d1.json);
+* with the rounding replaced by the identity, the tiled algorithm equals
+  exact attention (the prefill oracle) for any tile size;
+* when every probability is a power of two (exactly representable), the
+  8-bit result equals exact attention;
+* rounding P changes the result (the fp8 path is not silently exact).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn_fwd
+from oracle.fp8 import E4M3_MAX, attn_fwd_fp8, e4m3_values, quantize_e4m3, round_e4m3
+from test_oracle import _arr
+
+
+def _torch_e4m3(x):
+    return torch.tensor(np.asarray(x, dtype=np.float64)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_code_table_matches_torch():
+    mine = np.sort(e4m3_values())
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(mine, np.sort(t[~np.isnan(t)]))
+    assert mine.max() == E4M3_MAX and mine.min() == -E4M3_MAX
+
+
+def test_rounding_matches_torch_on_random_values():
+    g = np.random.default_rng(7)
+    x = g.standard_normal(100000) * np.exp2(g.uniform(-14, 9, 100000))
+    x = x[np.abs(x) < E4M3_MAX]
+    assert np.array_equal(round_e4m3(x), _torch_e4m3(x))
+
+
+def test_rounding_special_cases():
+    cases = [1.0 + 1 / 16, 1.0 + 3 / 16, 0.5 + 1 / 64, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -9, 2.0 ** -6,
+             -(1.0 + 1 / 16), 447.0, 440.0, 0.0, 1 / 3, 17.0, 19.0]
+    expect = [1.0, 1.25, 0.5, 0.0, 2.0 ** -8, 2.0 ** -9, 2.0 ** -6, -1.0, 448.0, 448.0, 0.0, 11 / 32, 16.0, 20.0]
+    assert list(round_e4m3(cases)) == expect
+    assert np.array_equal(round_e4m3(cases[:-1]), _torch_e4m3(cases[:-1]))
+    assert round_e4m3([1000.0, -1000.0]).tolist() == [448.0, -448.0]   # saturation
+
+
+def test_quantize_roundtrip_bound():
+    x = np.random.default_rng(3).standard_normal(5000) * 3.0
+    q8, ds = quantize_e4m3(x)
+    assert np.abs(q8).max() <= E4M3_MAX and float(np.float32(ds)) == ds
+    # Relative error of a normal E4M3 value is at most 2^-4.
+    big = np.abs(x / ds) >= 2.0 ** -6
+    assert np.all(np.abs(q8[big] * ds - x[big]) <= 2.0 ** -4 * np.abs(x[big]) + 1e-12)
+
+
+@pytest.mark.parametrize("mask", ["noncausal", "causal"])
+def test_golden_fp8(golden_dir, mask):
+    with open(os.path.join(golden_dir, "hand_fp8_n2_d1.json")) as f:
+        g = json.load(f)
+    q = np.array(_arr(g["q"])).reshape(1, 2, 1, 1)
+    k = np.array(_arr(g["k"])).reshape(1, 2, 1, 1)
+    v = np.array(_arr(g["v"])).reshape(1, 2, 1, 1)
+    # The fixture's inputs are the dequantised values: descales 1.
+    o, lse = attn_fwd_fp8(q, k, v, 1.0, 1.0, 1.0, mask == "causal", float(_arr(g["scale"])))
+    e = g["expected"][mask]
+    assert np.allclose(o[0, :, 0, 0], np.array(_arr(e["o"]))[:, 0], rtol=0, atol=1e-14)
+    assert np.allclose(lse[0, 0], np.array(_arr(e["lse"])), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("tile", [1, 7, 64, 200])
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_rounding_is_exact_attention(tile, causal):
+    g = np.random.default_rng(11)
+    q, k, v = (g.standard_normal((2, 150, 3, 8)) for _ in range(3))
+    o, lse = attn_fwd_fp8(q, k, v, 0.5, 2.0, 1.5, causal, 0.3, tile=tile, round_p=lambda p: p)
+    ro, rl = attn_fwd(q * 0.5, k * 2.0, v * 1.5, causal, 0.3)
+    assert np.abs(o - ro).max() <= 1e-12 and np.abs(lse - rl).max() <= 1e-12
+
+
+def test_power_of_two_probabilities_are_exact():
+    # d = 1, q = 1, scale 1: scores are the keys; keys -n ln 2 give P = 2^-n (exact in E4M3 for n <= 9),
+    # and the first key (score 0) is every row's maximum, in the first tile.
+    n = 100
+    e = np.random.default_rng(5).integers(0, 9, size=n)
+    e[0] = 0
+    k = (-e * np.log(2.0)).reshape(1, n, 1, 1)
+    q = np.ones((1, n, 1, 1))
+    v = np.random.default_rng(6).standard_normal((1, n, 1, 1))
+    for causal in (False, True):
+        o, lse = attn_fwd_fp8(q, k, v, 1.0, 1.0, 1.0, causal, 1.0)
+        ro, rl = attn_fwd(q, k, v, causal, 1.0)
+        assert np.abs(o - ro).max() <= 1e-12 and np.abs(lse - rl).max() <= 1e-12
+
+
+def test_rounding_p_changes_the_result():
+    g = np.random.default_rng(9)
+    q, k, v = (g.standard_normal((1, 80, 2, 16)) for _ in range(3))
+    o8, l8 = attn_fwd_fp8(q, k, v, 1.0, 1.0, 1.0, False, 0.25)
+    ro, rl = attn_fwd(q, k, v, False, 0.25)
+    assert np.abs(o8 - ro).max() > 1e-4          # O sees the 8-bit P
+    assert np.abs(l8 - rl).max() <= 1e-12        # LSE uses the unrounded P
