@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     attn_decode_workspace_size,
     attn_fwd,
     attn_fwd_fp32,
+    attn_fwd_fp8,
     attn_fwd_gqa,
     default_scale,
     lib,

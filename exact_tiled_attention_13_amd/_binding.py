@@ -25,7 +25,7 @@ FA_ERR_HIP = 4
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_prep",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_gqa", "attn_bwd_gqa", "attn_decode_workspace_size",
-            "attn_decode", "fa_status_string")
+            "attn_decode", "attn_fwd_fp8", "fa_status_string")
 
 _lock = threading.Lock()
 _lib = None
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
             L.attn_decode_workspace_size.restype = sz
             L.attn_decode.argtypes = [vp] * 5 + [vp, sz] + [ci, ci, ci, ci, ci, ci, ci, cf, vp]
             L.attn_decode.restype = ci
+            L.attn_fwd_fp8.argtypes = [vp, vp, vp, ci, cf, cf, cf, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+            L.attn_fwd_fp8.restype = ci
             L.fa_status_string.argtypes = [ci]
             L.fa_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -307,4 +309,34 @@ def attn_decode(q, k, v, causal: bool = False, scale: float | None = None, o=Non
     s = default_scale(d) if scale is None else float(scale)
     _check("attn_decode", lib().attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), _nbytes(ws),
                                             B, H, Hkv, Nq, Nk, d, int(bool(causal)), s, _stream(dev)))
+    return o, lse
+
+
+def _bytes8(name, t, shape, device):
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8) or tuple(t.shape) != tuple(shape) \
+            or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous float8_e4m3fn (or uint8) {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def attn_fwd_fp8(q8, k8, vt8, q_descale: float, k_descale: float, v_descale: float, causal: bool = False,
+                 scale: float | None = None, o=None, lse=None):
+    """FP8 (E4M3) forward. q8, k8 [B, N, H, d]; vt8 = V transposed per head [B, H, d, ldv] (keys
+    contiguous, zero padding past N, ldv a multiple of 64 covering N). Returns (o bf16, lse fp32)."""
+    B, N, H, d = _shape(q8)
+    dev = q8.device
+    _bytes8("q8", q8, (B, N, H, d), dev)
+    _bytes8("k8", k8, (B, N, H, d), dev)
+    if vt8.dim() != 4:
+        raise ValueError(f"vt8: expected [B, H, d, ldv], got {tuple(vt8.shape)}")
+    ldv = int(vt8.shape[3])
+    _bytes8("vt8", vt8, (B, H, d, ldv), dev)
+    o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _expect("o", o, (B, N, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    s = default_scale(d) if scale is None else float(scale)
+    _check("attn_fwd_fp8", lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), ldv, float(q_descale),
+                                              float(k_descale), float(v_descale), _ptr(o), _ptr(lse), B, H, N, d,
+                                              int(bool(causal)), s, _stream(dev)))
     return o, lse

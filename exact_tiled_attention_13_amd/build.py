@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa_mi355x.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_fp32.hip", "bwd_bf16.hip", "decode_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_fp32.hip", "fwd_fp8.hip", "bwd_bf16.hip", "decode_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -39,7 +39,8 @@ FLAGS = [
 # softmax then copies S and dP back to VGPRs each tile. The VGPR form keeps
 # S / dP in VGPRs (the accumulators that do not fit spill to AGPRs instead).
 EXTRA_FLAGS = {"bwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
-               "decode_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+               "decode_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+               "fwd_fp8.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

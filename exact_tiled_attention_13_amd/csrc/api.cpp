@@ -83,6 +83,31 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
 }
 
+int attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, int ldv, float q_descale, float k_descale,
+                 float v_descale, void* o, float* lse, int B, int H, int N, int d, int causal, float scale,
+                 hipStream_t stream) {
+    int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    const float descales[3] = {q_descale, k_descale, v_descale};
+    for (float x : descales)
+        if (!isfinite(x) || !(x > 0.0f)) return FA_ERR_INVALID_ARG;
+    if (ldv < (N + 63) / 64 * 64 || ldv % 16 != 0) return FA_ERR_INVALID_ARG;
+    if ((long long)B * H * d * (long long)ldv >= (1LL << 40)) return FA_ERR_INVALID_ARG;
+    st = check_ptrs({q8, k8, vt8, o, lse});
+    if (st != FA_OK) return st;
+    fa::Fp8Args a{};
+    a.q = q8; a.k = k8; a.vt = vt8; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.N = N; a.ldv = ldv;
+    const float eff = scale * q_descale * k_descale;
+    float unused_f;
+    uint32_t unused_s;
+    fill_scale(eff, a.c2, unused_s, unused_f);
+    a.qsign = (signbit(eff) && eff != 0.0f) ? 0x80808080u : 0u;
+    a.dv = v_descale;
+    return fa::launch_fwd_fp8(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int attn_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
                   int d, int causal, float scale, hipStream_t stream) {
     int st = check_shape(B, H, N, d, scale);

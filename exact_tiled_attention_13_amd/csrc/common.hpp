@@ -61,6 +61,22 @@ struct BwdArgs {
     uint32_t qsign;   // as in FwdArgs
 };
 
+// Launch arguments of the FP8 forward. q, k are E4M3 bytes [B, N, H, d]; vt is
+// V transposed per head, E4M3 bytes [B, H, d, ldv] (keys contiguous, keys N ..
+// ldv-1 of each row finite padding); o bf16 [B, N, H, d]; lse [B, H, N].
+struct Fp8Args {
+    const void* q;
+    const void* k;
+    const void* vt;
+    void* o;
+    float* lse;
+    int B, H, N;
+    int ldv;          // bytes per V^T row, a multiple of 64 and at least N
+    float c2;         // |scale * q_descale * k_descale| * log2(e)
+    uint32_t qsign;   // 0x80808080 when that product is negative (folded into Q's sign bits), else 0
+    float dv;         // V descale: O = (P V8) * dv / l
+};
+
 // Launch arguments of the decoding kernels. q, o are [B, Nq, H, d]; k, v the
 // cache [B, Nk, Hkv, d]; lse [B, H, Nq]. Query row r (0 <= r < R) of K/V head
 // hk is query i = r / G of head hk * G + r % G, G = H / Hkv.

@@ -113,6 +113,28 @@ def make_decode(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int = 
     return tuple(out)
 
 
+def make_fp8(B: int, H: int, N: int, d: int, seed: int = 0):
+    """FP8 inputs on the CPU: Q, K, V drawn as make_qkv draws them (randn float32), each quantised per tensor
+    to E4M3 with descale = amax / 448 (rounded to fp32) by torch's float8_e4m3fn conversion (nearest even).
+    Returns (q8, k8, v8 [B, N, H, d] float8_e4m3fn, vt8 [B, H, d, ldv] uint8 with zero padding,
+    (q_descale, k_descale, v_descale))."""
+    g = torch.Generator().manual_seed(seed)
+    out, ds = [], []
+    for _ in range(3):
+        x = torch.randn(B, N, H, d, dtype=torch.float32, generator=g)
+        s = float(torch.tensor(float(x.abs().max()) / 448.0, dtype=torch.float32))
+        out.append((x / s).to(torch.float8_e4m3fn))
+        ds.append(s)
+    ldv = (N + 63) // 64 * 64
+    vt8 = torch.zeros(B, H, d, ldv, dtype=torch.uint8)
+    vt8[..., :N] = out[2].view(torch.uint8).permute(0, 2, 3, 1)
+    return out[0], out[1], out[2], vt8.contiguous(), tuple(ds)
+
+
+# The FP8 forward at the long-context shape (reported beside the bf16 step).
+FP8_LONG = Workload("fwd_fp8_b1_h16_n16384_d128", "fp8", 1, 16, 16384, 128, (False, True), False, 1010)
+
+
 def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0, with_do: bool = False):
     """Draw Q, K, V (and dO) on the CPU. Returns a tuple of CPU tensors [B, N, H, d].
 

@@ -174,6 +174,31 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, con
                 hipStream_t stream);
 
 /*
+ * attn_fwd_fp8 -- FP8 (OCP E4M3) forward (page "FlashAttention-T: Optimización
+ * GPU para LLMs Escalables", section "Innovaciones técnicas frente a
+ * FlashAttention original", which names 8-bit quantisation as supported):
+ *   q8, k8   E4M3 bytes, [B, N, H, d], device, read-only.
+ *   vt8      V transposed per head, E4M3 bytes, [B, H, d, ldv]: row (b, h, c)
+ *            holds V[b, :, h, c] for keys 0 .. N-1 contiguously; bytes N ..
+ *            ldv-1 of each row are read and must hold finite values (zero).
+ *   ldv      bytes per vt8 row: a multiple of 16 and at least 64 * ceil(N/64).
+ *   q_descale, k_descale, v_descale: per-tensor factors, finite and > 0; the
+ *            real inputs are value * descale.
+ *   o        output [B, N, H, d] bf16; lse output [B, H, N] fp32 (natural log).
+ *   d        must be 128.
+ * Scores S = scale * (q8 * q_descale)(k8 * k_descale)^T are exact products of
+ * E4M3 values summed in fp32; the online softmax keeps the exact running
+ * maximum over 64-key tiles, so P = exp(S - m) <= 1; P is rounded to E4M3
+ * (nearest even) for the P V product while the row sum l and LSE use the
+ * unrounded P; O = v_descale * (sum of rescaled E4M3(P) V8) / l.
+ * Errors: as attn_fwd, plus FA_ERR_INVALID_ARG for a descale that is not
+ * finite and positive or a bad ldv, and FA_ERR_UNSUPPORTED for d != 128.
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, int ldv,
+                 float q_descale, float k_descale, float v_descale, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
  * Decoding against a key/value cache (page "FlashAttention-2: atención
  * eficiente en GPU para contextos largos", section "Cómo documentar una
  * diferencia técnica", which separates the first pass over a context from

@@ -69,16 +69,33 @@ def e4m3_values() -> np.ndarray:
     return np.array(vals)
 
 
-def attn_fwd_fp8_head(q, k, v, causal: bool, scale: float, tile: int = 64, round_p=round_e4m3):
-    """One head: q [N, d], k [N, d], v [N, d] (dequantised values) -> (O [N, d], LSE [N])."""
+def attn_fwd_fp8_head(q, k, v, causal: bool, scale: float, tile: int = 64, round_p=round_e4m3,
+                      flip_eta: float | None = None):
+    """One head: q [N, d], k [N, d], v [N, d] (dequantised values) -> (O [N, d], LSE [N]).
+
+    With ``flip_eta`` set, also returns a bound [N, d] on how far O moves if
+    every probability within a relative ``flip_eta`` of an E4M3 rounding
+    boundary rounds to the other neighbour instead (an implementation that
+    computes P with a relative error below flip_eta can only differ from
+    this oracle in those roundings): the sum over such keys of
+    |E4M3(P (1 + eta)) - E4M3(P (1 - eta))| |v|, rescaled to the final
+    maximum and divided by l. ``flip_eta="fp32"`` derives eta per row for
+    scores accumulated on the FP8 matrix cores (see fp32_p_error) and adds
+    the error of evaluating the rest that way: MFMA_FP8_GAMMA_SCALE gamma_n
+    sum_j E4M3(P_j) |v_j| / l for the P V sums, gamma_n |O| for the fp32 row
+    sum l (n = N + 2 terms each), and eta |O| because l sums the unrounded P.
+    """
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     n = q.shape[0]
     s_all = scale * (q @ k.T)
     if causal:
         s_all = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], s_all, -np.inf)
+    eta = fp32_p_error(q, k, scale) if isinstance(flip_eta, str) else flip_eta
     m = np.full(n, -np.inf)
     l = np.zeros(n)
     acc = np.zeros((n, v.shape[1]))
+    flip = np.zeros_like(acc)
+    accabs = np.zeros_like(acc)
     for t0 in range(0, n, tile):
         s = s_all[:, t0:t0 + tile]
         mt = s.max(axis=1)
@@ -88,21 +105,69 @@ def attn_fwd_fp8_head(q, k, v, causal: bool, scale: float, tile: int = 64, round
         p = np.exp(s - safe[:, None])          # masked keys: exp(-inf) = 0
         l = l * alpha + p.sum(axis=1)
         acc = acc * alpha[:, None] + round_p(p) @ v[t0:t0 + tile]
+        if flip_eta is not None:
+            e_row = np.broadcast_to(np.asarray(eta, dtype=np.float64).reshape(-1, 1) if np.ndim(eta) else eta,
+                                    p.shape)
+            gap = np.abs(round_e4m3(p * (1 + e_row)) - round_e4m3(p * (1 - e_row)))
+            flip = flip * alpha[:, None] + gap @ np.abs(v[t0:t0 + tile])
+            accabs = accabs * alpha[:, None] + round_p(p) @ np.abs(v[t0:t0 + tile])
         m = mn
-    return acc / l[:, None], m + np.log(l)
+    o = acc / l[:, None]
+    if flip_eta is not None:
+        bound = flip / l[:, None]
+        if isinstance(flip_eta, str):
+            u = 2.0 ** -24
+            g = (n + 2) * u / (1 - (n + 2) * u)
+            # l sums the unrounded P, whose relative error (eta) reaches O unchanged.
+            bound = bound + g * (MFMA_FP8_GAMMA_SCALE * accabs / l[:, None] + np.abs(o)) \
+                + np.asarray(eta).reshape(-1, 1) * np.abs(o)
+        return o, m + np.log(l), bound
+    return o, m + np.log(l)
+
+
+# Sums of products formed on gfx950's FP8 matrix cores err by more than a
+# sequential fp32 sum: a probe of v_mfma_f32_32x32x64_f8f6f4 measured up to
+# 2.3 gamma_64 sum |a_i b_i| (gamma_n = n u / (1 - n u), u = 2^-24). The bounds
+# below scale gamma by this factor for such sums.
+MFMA_FP8_GAMMA_SCALE = 8.0
+
+
+def fp32_p_error(q, k, scale: float, gamma_scale: float = MFMA_FP8_GAMMA_SCALE) -> np.ndarray:
+    """Per query row, a bound on the relative error of P = exp(S - m) when the scores are d-term dot products
+    accumulated in fp32 (unit roundoff u = 2^-24; gamma scaled by ``gamma_scale`` for sums formed on the FP8
+    matrix cores, 1 for a sequential fp32 sum) and scaled by an fp32 factor, and exp is evaluated in fp32.
+
+    The standard bound |fl(sum a_i b_i) - sum a_i b_i| <= gamma_d sum |a_i b_i| (gamma_d = d u / (1 - d u))
+    gives each score an absolute error e_j <= |scale| (gamma_d sum_i |q_i k_ji| + 4 u |sum_i q_i k_ji|); the
+    exponent S_j - m then errs by at most 2 max_j e_j (m is itself one of the perturbed scores), and the
+    fp32 exponential adds a few units: eta = exp(2 max_j e_j) (1 + 8 u) - 1.
+    """
+    q, k = np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64)
+    u = 2.0 ** -24
+    dd = q.shape[1]
+    gamma = dd * u / (1 - dd * u)
+    e = abs(scale) * (gamma_scale * gamma * (np.abs(q) @ np.abs(k).T) + 4 * u * np.abs(q @ k.T))
+    return np.expm1(2 * e.max(axis=1)) * (1 + 8 * u) + 8 * u
 
 
 def attn_fwd_fp8(q8, k8, v8, dq: float, dk: float, dv: float, causal: bool, scale: float, tile: int = 64,
-                 round_p=round_e4m3):
-    """q8, k8, v8: e4m3 values (already representable) [B, N, H, d]; returns (O [B, N, H, d], LSE [B, H, N])."""
+                 round_p=round_e4m3, flip_eta: float | None = None):
+    """q8, k8, v8: e4m3 values (already representable) [B, N, H, d]; returns (O [B, N, H, d], LSE [B, H, N]),
+    plus the rounding-flip bound [B, N, H, d] of attn_fwd_fp8_head when ``flip_eta`` is set."""
     q8, k8, v8 = (np.asarray(t, dtype=np.float64) for t in (q8, k8, v8))
     B, N, H, d = q8.shape
     o = np.empty((B, N, H, d))
     lse = np.empty((B, H, N))
+    bound = np.zeros((B, N, H, d))
     for b in range(B):
         for h in range(H):
-            o[b, :, h], lse[b, h] = attn_fwd_fp8_head(q8[b, :, h] * dq, k8[b, :, h] * dk, v8[b, :, h] * dv,
-                                                      causal, scale, tile, round_p)
+            r = attn_fwd_fp8_head(q8[b, :, h] * dq, k8[b, :, h] * dk, v8[b, :, h] * dv, causal, scale, tile,
+                                  round_p, flip_eta)
+            o[b, :, h], lse[b, h] = r[0], r[1]
+            if flip_eta is not None:
+                bound[b, :, h] = r[2]
+    if flip_eta is not None:
+        return o, lse, bound
     return o, lse
 
 
@@ -124,4 +189,4 @@ def flops_fwd_fp8(B: int, H: int, N: int, d: int, causal: bool) -> float:
 
 
 __all__ = ["E4M3_MAX", "round_e4m3", "e4m3_values", "attn_fwd_fp8_head", "attn_fwd_fp8", "quantize_e4m3",
-           "flops_fwd_fp8"]
+           "flops_fwd_fp8", "fp32_p_error"]

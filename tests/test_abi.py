@@ -162,3 +162,20 @@ def test_decode_rejects_bad_arguments():
     assert dec(ws=0) == fa.FA_ERR_WORKSPACE
     assert dec(ws=MIS) == fa.FA_ERR_WORKSPACE
     assert dec(wsb=16) == fa.FA_ERR_WORKSPACE
+
+
+def f8(q=P, k=P, vt=P, ldv=128, dq=1.0, dk=1.0, dv=1.0, o=P, lse=P, B=1, H=2, N=100, d=128, causal=0, scale=0.1):
+    return fa.lib().attn_fwd_fp8(q, k, vt, ldv, dq, dk, dv, o, lse, B, H, N, d, causal, scale, None)
+
+
+def test_fp8_rejects_bad_arguments():
+    assert f8(q=0) == fa.FA_ERR_INVALID_ARG
+    assert f8(vt=MIS) == fa.FA_ERR_INVALID_ARG
+    assert f8(N=0) == fa.FA_ERR_INVALID_ARG
+    assert f8(dq=0.0) == fa.FA_ERR_INVALID_ARG
+    assert f8(dk=-1.0) == fa.FA_ERR_INVALID_ARG
+    assert f8(dv=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert f8(ldv=100) == fa.FA_ERR_INVALID_ARG        # fewer than 64 * ceil(N / 64) bytes per row
+    assert f8(ldv=136, N=100) == fa.FA_ERR_INVALID_ARG  # ldv = 136 covers N but is not a multiple of 16... (136 % 16 = 8)
+    assert f8(scale=float("inf")) == fa.FA_ERR_INVALID_ARG
+    assert f8(d=64) == fa.FA_ERR_UNSUPPORTED

@@ -105,3 +105,47 @@ def test_rounding_p_changes_the_result():
     ro, rl = attn_fwd(q, k, v, False, 0.25)
     assert np.abs(o8 - ro).max() > 1e-4          # O sees the 8-bit P
     assert np.abs(l8 - rl).max() <= 1e-12        # LSE uses the unrounded P
+
+
+def test_flip_bound_contains_every_alternative_rounding():
+    # Perturb P by a relative 1e-6 before rounding (as an fp32 implementation might): the result moves by
+    # no more than the bound computed with eta = 1e-5, element by element.
+    g = np.random.default_rng(21)
+    q, k, v = (g.standard_normal((1, 300, 2, 16)) for _ in range(3))
+    o, lse, bound = attn_fwd_fp8(q, k, v, 1.0, 1.0, 1.0, True, 0.25, flip_eta=1e-5)
+    for seed in range(3):
+        rng = np.random.default_rng(100 + seed)
+        jitter = lambda p: round_e4m3(p * (1 + 1e-6 * rng.uniform(-1, 1, p.shape)))
+        o2, _ = attn_fwd_fp8(q, k, v, 1.0, 1.0, 1.0, True, 0.25, round_p=jitter)
+        assert np.all(np.abs(o2 - o) <= bound + 1e-12)
+    assert bound.max() > 0 and bound.mean() < 1e-2 * np.abs(o).mean()
+
+
+def test_flip_bound_zero_for_exact_probabilities():
+    n = 64
+    e = np.random.default_rng(5).integers(0, 9, size=n)
+    e[0] = 0
+    k = (-e * np.log(2.0)).reshape(1, n, 1, 1)
+    q = np.ones((1, n, 1, 1))
+    v = np.random.default_rng(6).standard_normal((1, n, 1, 1))
+    _, _, bound = attn_fwd_fp8(q, k, v, 1.0, 1.0, 1.0, False, 1.0, flip_eta=1e-5)
+    assert bound.max() < 1e-12
+
+
+def test_fp32_p_error_bounds_an_fp32_evaluation():
+    # Scores accumulated in fp32 in a random order, scaled and exponentiated in fp32: the relative error of
+    # P against fp64 stays below the bound.
+    from oracle.fp8 import fp32_p_error
+    g = np.random.default_rng(31)
+    q = round_e4m3(g.standard_normal((40, 128)) * 100)
+    k = round_e4m3(g.standard_normal((70, 128)) * 100)
+    scale = 1.3e-5
+    s64 = scale * (q @ k.T)
+    p64 = np.exp(s64 - s64.max(axis=1, keepdims=True))
+    qk32 = np.zeros((40, 70), dtype=np.float32)
+    for i in g.permutation(128):
+        qk32 = (qk32 + (q[:, i:i + 1] * k[:, i][None, :]).astype(np.float32)).astype(np.float32)
+    s32 = (qk32 * np.float32(scale)).astype(np.float32)
+    p32 = np.exp((s32 - s32.max(axis=1, keepdims=True)).astype(np.float32)).astype(np.float64)
+    rel = np.abs(p32 - p64) / p64
+    assert np.all(rel.max(axis=1) <= fp32_p_error(q, k, scale, gamma_scale=1.0))
