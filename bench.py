@@ -174,6 +174,39 @@ def time_decode(w, reps=20, warmup=5):
     return out
 
 
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
+
+
+def time_fp8(w, reps=10, warmup=3):
+    """Report-only timing of the FP8 (E4M3) forward at a workload's shape, both of its masks; counted FLOP
+    as for the bf16 forward, against the fp8 and the bf16 dense peaks."""
+    import torch
+
+    import exact_tiled_attention_13_amd as fa
+    from exact_tiled_attention_13_amd.inputs import make_fp8
+
+    dev = torch.device("cuda:0")
+    q8, k8, _, vt8, ds = make_fp8(w.B, w.H, w.N, w.d, w.seed)
+    q8, k8, vt8 = q8.to(dev), k8.to(dev), vt8.to(dev)
+    out = {}
+    for c in w.causal:
+        o, lse = fa.attn_fwd_fp8(q8, k8, vt8, *ds, c, w.scale)
+        for _ in range(warmup):
+            fa.attn_fwd_fp8(q8, k8, vt8, *ds, c, w.scale, o=o, lse=lse)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fa.attn_fwd_fp8(q8, k8, vt8, *ds, c, w.scale, o=o, lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = counted_fwd(w.B, w.H, w.N, w.d, c) / ms / 1e9
+        out["fwd_fp8_" + ("causal" if c else "noncausal")] = {
+            "ms": round(ms, 4), "tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,8 +352,8 @@ def main():
     }
     # Report-only: the other 16k-token workloads (head dim 64 at 16k tokens,
     # grouped-query attention at 16k tokens, the short-sequence and mid-length
-    # configurations, the batched backward) and decoding against a 16k-token
-    # cache (HBM-bound: reported in GB/s).
+    # configurations, the batched backward), decoding against a 16k-token
+    # cache (HBM-bound: reported in GB/s) and the FP8 forward at 16k tokens.
     from exact_tiled_attention_13_amd.inputs import LONG_D64, LONG_GQA, WORKLOADS
 
     if not args.no_report:
@@ -331,6 +364,9 @@ def main():
 
         for dw in (DECODE_1, DECODE_4):
             report[dw.name] = time_decode(dw)
+        from exact_tiled_attention_13_amd.inputs import FP8_LONG
+
+        report[FP8_LONG.name] = time_fp8(FP8_LONG)
         out["other_workloads"] = report
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale)
