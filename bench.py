@@ -120,7 +120,8 @@ def time_passes(w, reps=10, warmup=3):
         o, lse = fwd(q, k, v, c, w.scale)
         calls = {"fwd": (lambda: fwd(q, k, v, c, w.scale, o=o, lse=lse), 1.0)}
         if w.backward:
-            ws = fa.workspace(w.B, w.H, w.N, w.d, dev)
+            ws = (fa.workspace_gqa(w.B, w.H, w.kv_heads, w.N, w.d, c, dev) if gqa
+                  else fa.workspace(w.B, w.H, w.N, w.d, dev))
             dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
             calls["bwd"] = (lambda: bwd(q, k, v, o, xs[3], lse, c, w.scale, dq=dq, dk=dk, dv=dv,
                                         workspace=ws), 2.5)

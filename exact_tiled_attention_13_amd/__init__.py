@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_dkdv,
     attn_bwd_dq,
     attn_bwd_gqa,
+    attn_bwd_gqa_workspace_size,
     attn_bwd_prep,
     attn_bwd_workspace_size,
     attn_decode,
@@ -31,4 +32,5 @@ from ._binding import (  # noqa: F401
     lib,
     status_string,
     workspace,
+    workspace_gqa,
 )

@@ -24,7 +24,8 @@ FA_ERR_WORKSPACE = 3
 FA_ERR_HIP = 4
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_prep",
-            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_gqa", "attn_bwd_gqa", "attn_decode_workspace_size",
+            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_size",
+            "attn_decode_workspace_size",
             "attn_decode", "attn_fwd_fp8", "fa_status_string")
 
 _lock = threading.Lock()
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
             L.attn_fwd_gqa.restype = ci
             L.attn_bwd_gqa.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, ci, cf, vp]
             L.attn_bwd_gqa.restype = ci
+            L.attn_bwd_gqa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+            L.attn_bwd_gqa_workspace_size.restype = sz
             L.attn_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
             L.attn_decode_workspace_size.restype = sz
             L.attn_decode.argtypes = [vp] * 5 + [vp, sz] + [ci, ci, ci, ci, ci, ci, ci, cf, vp]
@@ -189,6 +192,17 @@ def workspace(B: int, H: int, N: int, d: int, device) -> torch.Tensor:
     return torch.empty(attn_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=device)
 
 
+def attn_bwd_gqa_workspace_size(B: int, H: int, Hkv: int, N: int, d: int, causal: bool = False) -> int:
+    """Bytes of workspace that let attn_bwd_gqa split the query heads of a K/V head (0 if rejected)."""
+    return int(lib().attn_bwd_gqa_workspace_size(B, H, Hkv, N, d, int(bool(causal))))
+
+
+def workspace_gqa(B: int, H: int, Hkv: int, N: int, d: int, causal: bool, device) -> torch.Tensor:
+    """A workspace tensor of attn_bwd_gqa_workspace_size bytes (uint8) on `device`."""
+    return torch.empty(max(attn_bwd_gqa_workspace_size(B, H, Hkv, N, d, causal), 256), dtype=torch.uint8,
+                       device=device)
+
+
 def attn_bwd_prep(o, do, lse, ws=None):
     """Fill the backward workspace (D_i and LSE_i * log2 e). Returns the workspace."""
     B, N, H, d = _shape(o)
@@ -270,9 +284,8 @@ def attn_bwd_gqa(q, k, v, o, do, lse, causal: bool = False, scale: float | None 
     _expect("dq", dq, (B, N, H, d), torch.bfloat16, dev)
     for name, t in (("dk", dk), ("dv", dv)):
         _expect(name, t, (B, N, Hkv, d), torch.bfloat16, dev)
-    need = attn_bwd_workspace_size(B, H, N, d, causal)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = workspace_gqa(B, H, Hkv, N, d, causal, dev)
     s = default_scale(d) if scale is None else float(scale)
     _check("attn_bwd_gqa", lib().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                               _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace), B, H, Hkv,

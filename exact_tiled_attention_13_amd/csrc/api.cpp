@@ -59,6 +59,14 @@ int check_ws(const void* ws, size_t bytes, int B, int H, int N) {
     return FA_OK;
 }
 
+// Grouped-query backward: after the statistics, room for the fp32 partial
+// dK, dV of a split dK/dV stage ([S][2][B, N, Hkv, d]).
+size_t gqa_part_bytes(int B, int Hkv, int N, int d, int S) {
+    if (S <= 1) return 0;
+    const size_t raw = (size_t)S * 2 * (size_t)B * N * Hkv * d * sizeof(float);
+    return (raw + 255) & ~(size_t)255;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,6 +184,17 @@ int dkdv_stage(const void* q, const void* k, const void* v, const void* dO, cons
     st = check_ptrs({dk, dv});
     if (st != FA_OK) return st;
     a.dk = dk; a.dv = dv;
+    // Split the query heads of a K/V head when the caller's workspace has
+    // room for the partial sums (attn_bwd_gqa_workspace_size); else unsplit.
+    a.gsplit = 1;
+    if (Hkv != H) {
+        const int S = fa::dkdv_gqa_splits(B, H, Hkv, N, d, causal != 0);
+        const size_t base = ws_bytes(B, H, N);
+        if (S > 1 && workspace_bytes >= base + gqa_part_bytes(B, Hkv, N, d, S)) {
+            a.gsplit = S;
+            a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(const_cast<void*>(workspace)) + base);
+        }
+    }
     return fa::launch_bwd_dkdv(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -205,6 +224,12 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, con
                 size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal, float scale,
                 hipStream_t stream) {
     return dq_stage(q, k, v, dO, workspace, workspace_bytes, dq, B, H, H, N, d, causal, scale, stream);
+}
+
+size_t attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d, int causal) {
+    if (check_shape(B, H, N, d, 1.0f) != FA_OK || check_heads(H, Hkv) != FA_OK) return 0;
+    const int S = Hkv == H ? 1 : fa::dkdv_gqa_splits(B, H, Hkv, N, d, causal != 0);
+    return ws_bytes(B, H, N) + gqa_part_bytes(B, Hkv, N, d, S);
 }
 
 int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

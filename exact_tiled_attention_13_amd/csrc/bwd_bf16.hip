@@ -94,10 +94,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int npad = (N + 63) & ~63;
     const int Hkv = GQA ? a.Hkv : H;
     const int G = GQA ? H / Hkv : 1;     // query heads sharing this K/V head
+    // Grouped-query split: the G heads run as S workgroups of GS heads each,
+    // which write fp32 partial sums (reduced by bwd_dkdv_reduce_kernel).
+    const int S = GQA ? a.gsplit : 1;
+    const int GS = G / S;
     const int nk = (N + BK - 1) / BK;
-    const int r = xcd_remap(blockIdx.x, nk * B * Hkv);
-    const int bhk = r / nk;
-    const int kb = r - bhk * nk;         // causal: low key blocks see the most query tiles, so go first
+    const int r = xcd_remap(blockIdx.x, nk * B * Hkv * S);
+    const int unit = r / nk;
+    const int kb = r - unit * nk;        // causal: low key blocks see the most query tiles, so go first
+    const int bhk = GQA ? unit / S : unit;
+    const int sp = GQA ? unit - bhk * S : 0;   // part of the head group
     const int b = bhk / Hkv, hk = bhk - b * Hkv;
 
     const int tid = threadIdx.x;
@@ -109,14 +115,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const size_t rs = (size_t)H * D;                  // Q / dO row stride
     const size_t rskv = (size_t)Hkv * D;              // K / V / dK / dV row stride
     const size_t kvbase = ((size_t)b * N * Hkv + hk) * D;
-    // Query head g of the group is h = hk * G + g: its Q / dO start D
-    // elements after head g - 1's, its statistics npad floats after.
-    const size_t qbase = ((size_t)b * N * H + (size_t)hk * G) * D;
+    // Query head g of this workgroup's part is h = hk * G + sp * GS + g: its
+    // Q / dO start D elements after head g - 1's, its statistics npad floats after.
+    const size_t qbase = ((size_t)b * N * H + (size_t)hk * G + (size_t)sp * GS) * D;
     const __bf16* Qg0 = static_cast<const __bf16*>(a.q) + qbase;
     const __bf16* dOg0 = static_cast<const __bf16*>(a.dO) + qbase;
     const __bf16* Kg = static_cast<const __bf16*>(a.k) + kvbase;
     const __bf16* Vg = static_cast<const __bf16*>(a.v) + kvbase;
-    const size_t stat0 = ((size_t)b * H + (size_t)hk * G) * npad;
+    const size_t stat0 = ((size_t)b * H + (size_t)hk * G + (size_t)sp * GS) * npad;
 
     const int k0 = kb * BK;
     const int kw = k0 + wave * 32;       // first key of this wave
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     // Causal: only the first BK / BQ tiles (queries k0 .. k0+BK-1) straddle the
     // diagonal of this workgroup's keys; they run the masked variant, the
     // rest the variant without mask arithmetic.
-    // With grouped-query attention the G query heads of this K/V head are
+    // With grouped-query attention the GS query heads of this workgroup are
     // processed one after the other, all accumulating into the same dK, dV;
     // the staged tiles run through them as one sequence n = g * ntiles + t.
     const int t_split = CAUSAL ? min(ntiles, BK / BQ) : 0;
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             gn = g + 1;
             tn = 0;
         }
-        if (gn < G) dma(gn, tn, (n + 1) & 1);
+        if (gn < GS) dma(gn, tn, (n + 1) & 1);
     };
     dma(0, 0, 0);
     wait_dma();
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             __syncthreads();
         }
     } else {
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < GS; ++g) {
             const int n0 = g * ntiles;
             for (int t = 0; t < t_split; ++t) {
                 load_next(g, t, n0 + t);
@@ -346,6 +352,25 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
 
+    if (GQA && S > 1) {
+        // Partial sums of this part of the head group: fp32, dK unscaled.
+        if (myk < N) {
+            const size_t elems = (size_t)B * N * Hkv * D;
+            float* pk = a.part + (size_t)(2 * sp) * elems + kvbase + (size_t)myk * rskv;
+            float* pv = pk + elems;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = db * 32 + 8 * g + 4 * hi;
+                    st16f(pk + d0, f32x4{dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2],
+                                         dkacc[db][4 * g + 3]});
+                    st16f(pv + d0, f32x4{dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2],
+                                         dvacc[db][4 * g + 3]});
+                }
+        }
+        return;
+    }
     if (myk < N) {
         __bf16* dkrow = static_cast<__bf16*>(a.dk) + kvbase + (size_t)myk * rskv;
         __bf16* dvrow = static_cast<__bf16*>(a.dv) + kvbase + (size_t)myk * rskv;
@@ -417,10 +442,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     const int npad = (N + 63) & ~63;
     const int Hkv = GQA ? a.Hkv : H;
     const int G = GQA ? H / Hkv : 1;     // query heads sharing this K/V head
+    // Grouped-query split: the G heads run as S workgroups of GS heads each,
+    // which write fp32 partial sums (reduced by bwd_dkdv_reduce_kernel).
+    const int S = GQA ? a.gsplit : 1;
+    const int GS = G / S;
     const int nk = (N + BK - 1) / BK;
-    const int r = xcd_remap(blockIdx.x, nk * B * Hkv);
-    const int bhk = r / nk;
-    const int kb = r - bhk * nk;         // causal: low key blocks see the most query tiles, so go first
+    const int r = xcd_remap(blockIdx.x, nk * B * Hkv * S);
+    const int unit = r / nk;
+    const int kb = r - unit * nk;        // causal: low key blocks see the most query tiles, so go first
+    const int bhk = GQA ? unit / S : unit;
+    const int sp = GQA ? unit - bhk * S : 0;   // part of the head group
     const int b = bhk / Hkv, hk = bhk - b * Hkv;
 
     const int tid = threadIdx.x;
@@ -434,12 +465,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     const size_t rs = (size_t)H * D;                  // Q / dO row stride
     const size_t rskv = (size_t)Hkv * D;              // K / V / dK / dV row stride
     const size_t kvbase = ((size_t)b * N * Hkv + hk) * D;
-    // Query head g of the group is h = hk * G + g: its Q / dO start D
-    // elements after head g - 1's, its statistics npad floats after.
-    const size_t qbase = ((size_t)b * N * H + (size_t)hk * G) * D;
+    // Query head g of this workgroup's part is h = hk * G + sp * GS + g: its
+    // Q / dO start D elements after head g - 1's, its statistics npad floats after.
+    const size_t qbase = ((size_t)b * N * H + (size_t)hk * G + (size_t)sp * GS) * D;
     const __bf16* Qg0 = static_cast<const __bf16*>(a.q) + qbase;
     const __bf16* dOg0 = static_cast<const __bf16*>(a.dO) + qbase;
-    const size_t stat0 = ((size_t)b * H + (size_t)hk * G) * npad;
+    const size_t stat0 = ((size_t)b * H + (size_t)hk * G + (size_t)sp * GS) * npad;
 
     const int k0 = kb * BK;
     const int kw = k0 + kg * 32;         // first key of this wave
@@ -689,7 +720,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
             gn = g + 1;
             tn = 0;
         }
-        if (gn < G) dma(gn, tn, qs == 2 ? 0 : qs + 1, gs ^ 1);
+        if (gn < GS) dma(gn, tn, qs == 2 ? 0 : qs + 1, gs ^ 1);
     };
     dma(0, 0, 0, 0);
     wait_dma();
@@ -705,13 +736,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
             qs = qs == 2 ? 0 : qs + 1;
             ++n;
         };
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < GS; ++g) {
             for (int t = 0; t < t_split; ++t) step(g, t, std::true_type{});
             for (int t = t_split; t < ntiles; ++t) step(g, t, std::false_type{});
         }
     } else {
         bool prev = false;
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < GS; ++g) {
             for (int t = 0; t < ntiles; ++t) {
                 const int gs = n & 1;
                 dma_next(g, t, qs, gs);
@@ -727,6 +758,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         ds_step(0, qs == 0 ? 2 : qs - 1, (n - 1) & 1, prev, false);
     }
 
+    if (GQA && S > 1) {
+        // Partial sums of this part of the head group: fp32, dK unscaled.
+        if (myk < N) {
+            const size_t elems = (size_t)B * N * Hkv * D;
+            float* prow = a.part + (size_t)(2 * sp + (pwave ? 1 : 0)) * elems + kvbase + (size_t)myk * rskv;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    st16f(prow + db * 32 + 8 * g + 4 * hi,
+                          f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]});
+        }
+        return;
+    }
     if (myk < N) {
         __bf16* row = static_cast<__bf16*>(pwave ? a.dv : a.dk) + kvbase + (size_t)myk * rskv;
         const float sc = pwave ? 1.0f : a.scale;
@@ -928,6 +973,34 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
+// Split grouped-query dK/dV: sums the gsplit fp32 partials of each element in
+// part order (so the result is deterministic), multiplies dK by the scale and
+// rounds both to bf16. One thread per 8 consecutive elements of dK or dV.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a) {
+    const size_t elems = (size_t)a.B * a.N * a.Hkv * D;
+    const size_t n8 = elems / 8;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= 2 * n8) return;
+    const int role = i >= n8;            // 0: dK, 1: dV
+    const size_t e = (i - (size_t)role * n8) * 8;
+    const float* p = a.part + (size_t)role * elems + e;
+    f32x4 s0 = *reinterpret_cast<const f32x4*>(p);
+    f32x4 s1 = *reinterpret_cast<const f32x4*>(p + 4);
+    for (int sp = 1; sp < a.gsplit; ++sp) {
+        p += 2 * elems;
+        s0 += *reinterpret_cast<const f32x4*>(p);
+        s1 += *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    const float sc = role ? 1.0f : a.scale;
+    u32x4 w;
+    w[0] = pack_bf16x2(s0[0] * sc, s0[1] * sc);
+    w[1] = pack_bf16x2(s0[2] * sc, s0[3] * sc);
+    w[2] = pack_bf16x2(s1[0] * sc, s1[1] * sc);
+    w[3] = pack_bf16x2(s1[2] * sc, s1[3] * sc);
+    st16(static_cast<__bf16*>(role ? a.dv : a.dk) + e, w);
+}
+
 template <int D>
 static hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
     const long long rows = (long long)a.B * ((a.N + 63) & ~63) * a.H;
@@ -938,7 +1011,8 @@ static hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
-    const long long g = (long long)((a.N + 127) / 128) * a.B * a.Hkv;
+    const int S = a.Hkv == a.H ? 1 : a.gsplit;
+    const long long g = (long long)((a.N + 127) / 128) * a.B * a.Hkv * S;
     // d = 128: the 8-wave P / dS pair kernel (7-8% faster at 16k tokens).
     // d = 64: the 4-wave kernel, which already fits two workgroups per CU.
     if constexpr (D == 128) {
@@ -951,6 +1025,13 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3((unsigned)g), dim3(256), 0, stream, a);
         else
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)g), dim3(256), 0, stream, a);
+    }
+    if (S > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const long long threads = 2LL * a.B * a.N * a.Hkv * D / 8;
+        hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                           stream, a);
     }
     return hipGetLastError();
 }

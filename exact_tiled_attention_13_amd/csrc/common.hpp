@@ -54,6 +54,8 @@ struct BwdArgs {
     void* dv;
     float* dd;        // workspace: -D_i = -dO_i . O_i, fp32 [B, H, Npad]
     float* lse2;      // workspace: LSE_i * log2(e), fp32 [B, H, Npad] (+inf on padded rows)
+    float* part;      // workspace: fp32 partial dK (unscaled), dV [gsplit][2][B, N, Hkv, d], when gsplit > 1
+    int gsplit;       // grouped-query dK/dV: query heads of a K/V head split over this many workgroups
     int B, H, N;
     int Hkv;          // K/V heads, as in FwdArgs (k, v, dk, dv are [B, N, Hkv, d])
     float scale;      // the caller's scale (multiplies dQ and dK)
@@ -151,6 +153,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+__device__ __forceinline__ void st16f(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

@@ -134,10 +134,18 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * attn_fwd_gqa -- as attn_fwd, with k, v [B, N, Hkv, d] bf16; q, o
  *   [B, N, H, d]; lse [B, H, N].
  * attn_bwd_gqa -- as attn_bwd, with k, v, dk, dv [B, N, Hkv, d]: the gradient
- *   of a K/V head is the sum over the H / Hkv query heads that read it
- *   (accumulated in fp32 inside one workgroup, so the result is still
- *   deterministic). The workspace is attn_bwd_workspace_size(B, H, N, d,
- *   causal), sized by the query heads.
+ *   of a K/V head is the sum over the H / Hkv query heads that read it, in
+ *   fp32. The workspace must hold at least attn_bwd_workspace_size(B, H, N,
+ *   d, causal) bytes (sized by the query heads); then one workgroup sums all
+ *   H / Hkv heads. Given attn_bwd_gqa_workspace_size(B, H, Hkv, N, d, causal)
+ *   bytes, it may instead split the heads of a K/V head over S workgroups
+ *   that write fp32 partial dK, dV into the workspace, summed afterwards in a
+ *   fixed order (a shape with few K/V heads, above all under the causal mask,
+ *   otherwise leaves most of the chip idle). Either way the result is
+ *   deterministic; the two ways may differ in the last bit of dK, dV.
+ * attn_bwd_gqa_workspace_size -- bytes of workspace for the split form above
+ *   (equal to attn_bwd_workspace_size when this shape is not split); 0 for
+ *   arguments attn_bwd_gqa would reject.
  * Errors as for attn_fwd / attn_bwd, plus FA_ERR_INVALID_ARG when Hkv <= 0 or
  * H is not a multiple of Hkv.
  */
@@ -147,6 +155,7 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,
                  int B, int H, int Hkv, int N, int d, int causal, float scale, hipStream_t stream);
+size_t attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d, int causal);
 
 /*
  * The three stages attn_bwd runs, in order, on one stream. They are exported

@@ -131,6 +131,29 @@ def test_gqa_rejects_bad_head_counts():
     assert L.attn_bwd_gqa(*([P] * 6), 0, P, P, P, need, 1, 4, 2, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
 
 
+def test_gqa_workspace_size():
+    # Never below the unsplit workspace; equal to it when K/V heads = query heads
+    # or the grid is already large; a multiple of the fp32 partial dK, dV more
+    # when split; 0 for rejected arguments.
+    for B, H, Hkv, N, d, c in [(1, 16, 2, 16384, 128, 1), (1, 16, 2, 16384, 128, 0), (2, 8, 1, 17, 64, 0),
+                               (1, 8, 8, 4096, 128, 1), (16, 32, 8, 1024, 128, 1)]:
+        base = fa.attn_bwd_workspace_size(B, H, N, d, c)
+        full = fa.attn_bwd_gqa_workspace_size(B, H, Hkv, N, d, c)
+        assert full >= base > 0
+        part = 2 * B * N * Hkv * d * 4
+        extra = full - base
+        assert extra == 0 or (extra % part == 0 and (H // Hkv) % (extra // part) == 0 and extra // part > 1)
+        if Hkv == H:
+            assert full == base
+    # 16 query heads on 2 K/V heads at 16k tokens: one unsplit workgroup per CU
+    # under the causal mask would leave the first key block alone setting the time.
+    assert fa.attn_bwd_gqa_workspace_size(1, 16, 2, 16384, 128, 1) > fa.attn_bwd_workspace_size(1, 16, 16384, 128, 1)
+    assert fa.attn_bwd_gqa_workspace_size(1, 16, 2, 16384, 128, 0) == fa.attn_bwd_workspace_size(1, 16, 16384, 128, 0)
+    assert fa.attn_bwd_gqa_workspace_size(1, 4, 3, 16, 64, 0) == 0
+    assert fa.attn_bwd_gqa_workspace_size(1, 4, 2, 16, 96, 0) == 0
+    assert fa.attn_bwd_gqa_workspace_size(1, 4, 2, 0, 64, 0) == 0
+
+
 def dec(q=P, k=P, v=P, o=P, lse=P, ws=P, wsb=1 << 30, B=1, H=8, Hkv=2, Nq=1, Nk=100, d=128, causal=0, scale=0.1):
     return fa.lib().attn_decode(q, k, v, o, lse, ws, wsb, B, H, Hkv, Nq, Nk, d, causal, scale, None)
 
