@@ -122,24 +122,27 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Args a) {
     auto vbuf = [&](int i) { return smem + (2 + i) * TILE; };
 
     // Direct loads: wave load `inst` fills LDS bytes inst*1024 .. +1023; lane i
-    // fetches the global chunk that the swizzle places in slot i.
-    auto dma = [&](int t, unsigned char* __restrict__ kd, unsigned char* __restrict__ vd) {
+    // fetches the global chunk that the swizzle places in slot i. K runs one
+    // tile ahead of V (tile t's scores are computed during step t - 1).
+    auto dma_k = [&](int t, unsigned char* kd) {
 #pragma unroll
         for (int j = 0; j < IPW; ++j) {
             const int inst = wave + NW * j;
-            {
-                const int row = inst * (1024 / KRB) + lane / KCH;         // key row within the tile
-                const int c = (lane % KCH) ^ swk(row);
-                const int key = min(t * BN + row, N - 1);               // past N: clamped, masked later
-                __builtin_amdgcn_global_load_lds(Kg + (size_t)key * rs + 16 * c, (lds8_void_t*)(kd + inst * 1024),
-                                                 16, 0, 0);
-            }
-            {
-                const int row = inst * (1024 / VRB) + lane / 4;         // d row of V^T
-                const int c = (lane % 4) ^ swv(row);
-                __builtin_amdgcn_global_load_lds(Vg + (size_t)row * a.ldv + t * BN + 16 * c,
-                                                 (lds8_void_t*)(vd + inst * 1024), 16, 0, 0);
-            }
+            const int row = inst * (1024 / KRB) + lane / KCH;           // key row within the tile
+            const int c = (lane % KCH) ^ swk(row);
+            const int key = min(t * BN + row, N - 1);                   // past N: clamped, masked later
+            __builtin_amdgcn_global_load_lds(Kg + (size_t)key * rs + 16 * c, (lds8_void_t*)(kd + inst * 1024), 16,
+                                             0, 0);
+        }
+    };
+    auto dma_v = [&](int t, unsigned char* vd) {
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            const int inst = wave + NW * j;
+            const int row = inst * (1024 / VRB) + lane / 4;             // d row of V^T
+            const int c = (lane % 4) ^ swv(row);
+            __builtin_amdgcn_global_load_lds(Vg + (size_t)row * a.ldv + t * BN + 16 * c,
+                                             (lds8_void_t*)(vd + inst * 1024), 16, 0, 0);
         }
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
@@ -154,6 +157,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Args a) {
         const int row = db * 32 + l32;
         return row * VRB + (((2 * hi + s) ^ swv(row)) << 4);
     };
+    auto kread = [&](const unsigned char* Ks, int kb, int c) {
+        return join(*reinterpret_cast<const u32x4*>(Ks + koff(kb, c, 0)),
+                    *reinterpret_cast<const u32x4*>(Ks + koff(kb, c, 1)));
+    };
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -162,28 +169,30 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Args a) {
     float l = 0.f;         // running sum over this lane's keys (other half added at the end)
     const float c2 = a.c2;
 
-    auto step = [&](int t, const unsigned char* __restrict__ Ks, const unsigned char* __restrict__ Vs,
-                    auto masked_c) {
-        // Operand reads of the whole tile first.
-        i32x8 ka[2][DC], va[DB];
+    // Score MFMA i of a tile: block i % 2, d chunk i / 2 (two chains).
+    constexpr int NS = 2 * DC;
+    auto scores = [&](f32x16 (&s)[2], const unsigned char* Ks) {
+        i32x8 ka[NS];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < NS; ++i) ka[i] = kread(Ks, i % 2, i / 2);
+        s[0] = f32x16{};
+        s[1] = f32x16{};
 #pragma unroll
-            for (int c = 0; c < DC; ++c)
-                ka[kb][c] = join(*reinterpret_cast<const u32x4*>(Ks + koff(kb, c, 0)),
-                                 *reinterpret_cast<const u32x4*>(Ks + koff(kb, c, 1)));
+        for (int i = 0; i < NS; ++i) s[i % 2] = mfma_fp8(ka[i], qf[i / 2], s[i % 2]);
+    };
+
+    // Step t: the score MFMAs of tile t + 1 run interleaved with the softmax
+    // of tile t (mask, exact running max, rescale, then the exponentials,
+    // row sums and E4M3 packing in NS parts, one after each MFMA), then the
+    // PV MFMAs of tile t. Loads of K_{t+2} and V_{t+1} are in flight meanwhile.
+    auto step = [&](int t, f32x16 (&scur)[2], f32x16 (&snext)[2], auto masked_c) {
+        if (t + 2 < ntiles) dma_k(t + 2, kbuf(t & 1));
+        if (t + 1 < ntiles) dma_v(t + 1, vbuf((t + 1) & 1));
+        const unsigned char* Ks = kbuf((t + 1) & 1);   // K_{t+1} (stale past the last tile; unused)
+        i32x8 ka[NS];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            va[db] = join(*reinterpret_cast<const u32x4*>(Vs + voff(db, 0)),
-                          *reinterpret_cast<const u32x4*>(Vs + voff(db, 1)));
+        for (int i = 0; i < NS; ++i) ka[i] = kread(Ks, i % 2, i / 2);
         fence();
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < DC; ++c) s[kb] = mfma_fp8(ka[kb][c], qf[c], s[kb]);
-        }
         if constexpr (decltype(masked_c)::value) {
             // Key of element u of block kb is t*BN + kb*32 + 8*(u/4) + 4*hi + u%4.
             const int lim = CAUSAL ? min(N - 1, myq) : N - 1;
@@ -191,15 +200,16 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Args a) {
             for (int kb = 0; kb < 2; ++kb) {
                 const int thr = lim - (t * BN + kb * 32 + 4 * hi);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) s[kb][u] = (8 * (u >> 2) + (u & 3) > thr) ? -INFINITY : s[kb][u];
+                for (int u = 0; u < 16; ++u) scur[kb][u] = (8 * (u >> 2) + (u & 3) > thr) ? -INFINITY : scur[kb][u];
             }
         }
-        float mx = -INFINITY;
+        float mc[2] = {-INFINITY, -INFINITY};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int u = 0; u < 16; u += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kb][u]), s[kb][u + 1]);
-        mx = max_halves(mx) * c2;
+            for (int u = 0; u < 16; u += 2)
+                mc[(u / 2) % 2] = __builtin_fmaxf(__builtin_fmaxf(mc[(u / 2) % 2], scur[kb][u]), scur[kb][u + 1]);
+        const float mx = max_halves(__builtin_fmaxf(mc[0], mc[1])) * c2;
         // Exact running max: P <= 1 for the E4M3 rounding.
         const float mn = __builtin_fmaxf(m, mx);
         if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
@@ -210,21 +220,32 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Args a) {
             m = mn;
         }
         const float mu = (m == -INFINITY) ? 0.f : m;
+        fence();
         uint32_t pw[2][4];
-        float ls = 0.f;
+        float ls[2] = {0.f, 0.f};
+        // Part g (0 .. 7) of the softmax: elements 4 (g % 4) .. +3 of block g / 4.
+        auto part = [&](int g) {
+            const int kb = g / 4, gg = g % 4;
+            float p[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    p[e] = exp2_fast(__builtin_fmaf(s[kb][4 * g + e], c2, -mu));
-                    ls += p[e];
-                }
-                pw[kb][g] = pack_e4m3x4(p[0], p[1], p[2], p[3]);
+            for (int e = 0; e < 4; ++e) {
+                p[e] = exp2_fast(__builtin_fmaf(scur[kb][4 * gg + e], c2, -mu));
+                ls[g % 2] += p[e];
             }
-        l += ls;
+            pw[kb][gg] = pack_e4m3x4(p[0], p[1], p[2], p[3]);
+        };
+        snext[0] = f32x16{};
+        snext[1] = f32x16{};
+        constexpr int PPM = 8 / NS;                    // softmax parts per score MFMA
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            snext[i % 2] = mfma_fp8(ka[i], qf[i / 2], snext[i % 2]);
+            fence();
+#pragma unroll
+            for (int g = i * PPM; g < (i + 1) * PPM; ++g) part(g);
+            fence();
+        }
+        l += ls[0] + ls[1];
         // Lane half 0 keeps block 0 and takes the other half's block-0 keys;
         // lane half 1 the same for block 1. Key 32*hi + j is then byte j.
         i32x8 pb;
@@ -234,29 +255,62 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Args a) {
             pb[2 * g] = (int)sw[0];
             pb[2 * g + 1] = (int)sw[1];
         }
+        const unsigned char* Vs = vbuf(t & 1);
+        i32x8 va[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            va[db] = join(*reinterpret_cast<const u32x4*>(Vs + voff(db, 0)),
+                          *reinterpret_cast<const u32x4*>(Vs + voff(db, 1)));
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] = mfma_fp8(va[db], pb, oacc[db]);
         fence();
-    };
-
-    const int t_split = min(CAUSAL ? q0 / BN : ntiles, (N % BN) ? ntiles - 1 : ntiles);
-    auto idle = [&](int tt) { return CAUSAL && tt * BN > qw + 31; };
-    auto run = [&](int t, unsigned char* __restrict__ Kc, unsigned char* __restrict__ Vc,
-                   unsigned char* __restrict__ Kn, unsigned char* __restrict__ Vn) {
-        if (t + 1 < ntiles) dma(t + 1, Kn, Vn);
-        if (!idle(t)) {
-            if (t < t_split) step(t, Kc, Vc, std::false_type{});
-            else step(t, Kc, Vc, std::true_type{});
-        }
         wait_dma();
         __syncthreads();
     };
-    dma(0, kbuf(0), vbuf(0));
+
+    // Prologue: K_0, V_0 and K_1 into LDS, then the scores of tile 0.
+    dma_k(0, kbuf(0));
+    dma_v(0, vbuf(0));
+    if (ntiles > 1) dma_k(1, kbuf(1));
     wait_dma();
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int c = t & 1;
-        run(t, kbuf(c), vbuf(c), kbuf(c ^ 1), vbuf(c ^ 1));
+    f32x16 sa[2], sb[2];
+    scores(sa, kbuf(0));
+    __syncthreads();   // kbuf(0) receives K_2 in step 0
+
+    // Tiles before t_split need no mask for any wave; the rest run the masked
+    // variant. Under the causal mask a wave stops computing at the first tile
+    // whose keys all follow its last query, but keeps issuing its share of
+    // the loads and passing the barriers until the workgroup is done.
+    const int t_split = min(CAUSAL ? q0 / BN : ntiles, (N % BN) ? ntiles - 1 : ntiles);
+    auto idle = [&](int tt) { return CAUSAL && tt * BN > qw + 31; };
+    int t = 0;
+    for (; t + 1 < t_split; t += 2) {
+        step(t, sa, sb, std::false_type{});
+        step(t + 1, sb, sa, std::false_type{});
+    }
+    if (t < t_split) {
+        step(t, sa, sb, std::false_type{});
+        ++t;
+        sa[0] = sb[0];
+        sa[1] = sb[1];
+    }
+    for (; t < ntiles; t += 2) {
+        if (idle(t)) break;
+        step(t, sa, sb, std::true_type{});
+        if (t + 1 < ntiles) {
+            if (idle(t + 1)) {
+                ++t;
+                break;
+            }
+            step(t + 1, sb, sa, std::true_type{});
+        }
+    }
+    for (; t < ntiles; ++t) {
+        if (t + 2 < ntiles) dma_k(t + 2, kbuf(t & 1));
+        if (t + 1 < ntiles) dma_v(t + 1, vbuf((t + 1) & 1));
+        wait_dma();
+        __syncthreads();
     }
 
     const float lt = sum_halves(l);
