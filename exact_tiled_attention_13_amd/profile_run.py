@@ -1,10 +1,13 @@
 """Run one stage of the attention path a few times, for profilers.
 
 Usage: python -m exact_tiled_attention_13_amd.profile_run WHAT [--causal] [--reps R]
-WHAT is one of fwd, bwd_prep, bwd_dkdv, bwd_dq, step (all four), or copy
-(a plain device-to-device copy of 256 MiB through torch, used to calibrate
-the HBM byte counters: it reads and writes exactly 256 MiB per launch).
-Workload: batch 1, 16 heads, 16384 tokens, head dim 128, bf16, seeded inputs.
+WHAT is one of fwd, bwd_prep, bwd_dkdv, bwd_dq, step (all four), fp8, decode,
+or copy (a plain device-to-device copy of 256 MiB through torch, used to
+calibrate the HBM byte counters: it reads and writes exactly 256 MiB per
+launch).
+Workloads: batch 1, 16 heads, 16384 tokens, head dim 128, seeded inputs, bf16
+(fwd .. step) or E4M3 (fp8); decode: 16 sequences, 32 query heads on 8 K/V
+heads, one new token (four with --causal) against a 16384-token cache.
 """
 
 import argparse
@@ -18,7 +21,7 @@ if ROOT not in sys.path:
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq", "step", "copy"])
+    ap.add_argument("what", choices=["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq", "step", "fp8", "decode", "copy"])
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--reps", type=int, default=3)
     args = ap.parse_args()
@@ -36,6 +39,32 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print("copy done", flush=True)
+        return
+
+    if args.what == "fp8":
+        from exact_tiled_attention_13_amd.inputs import FP8_LONG, make_fp8
+
+        w = FP8_LONG
+        q8, k8, _, vt8, ds = make_fp8(w.B, w.H, w.N, w.d, w.seed)
+        q8, k8, vt8 = q8.to(dev), k8.to(dev), vt8.to(dev)
+        o, lse = fa.attn_fwd_fp8(q8, k8, vt8, *ds, args.causal, w.scale)
+        for _ in range(args.reps):
+            fa.attn_fwd_fp8(q8, k8, vt8, *ds, args.causal, w.scale, o=o, lse=lse)
+        torch.cuda.synchronize()
+        print(f"fp8 causal={args.causal} done", flush=True)
+        return
+    if args.what == "decode":
+        from exact_tiled_attention_13_amd.inputs import DECODE_1, DECODE_4, make_decode
+
+        w = DECODE_4 if args.causal else DECODE_1
+        q, k, v = (x.to(dev) for x in make_decode(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed))
+        o, lse = fa.attn_decode(q, k, v, args.causal, w.scale)
+        ws = torch.empty(max(fa.attn_decode_workspace_size(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d), 256),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(args.reps):
+            fa.attn_decode(q, k, v, args.causal, w.scale, o=o, lse=lse, ws=ws)
+        torch.cuda.synchronize()
+        print(f"decode causal={args.causal} done", flush=True)
         return
 
     w = BWD_LONG
