@@ -52,6 +52,20 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_stubs(lib: str) -> None:
+    """Fail if the host side of any kernel launch was left undefined.
+
+    hipcc can drop a kernel template's host launch stub without an error (a
+    device-only construct that the host pass rejects silently); the library
+    then links but fails to load. nm lists such stubs as undefined."""
+    r = subprocess.run(["nm", "-C", "--undefined-only", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{r.stderr}")
+    missing = [ln.strip() for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the host code:\n" + "\n".join(missing))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library. Returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -62,6 +76,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    _check_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -73,7 +73,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     // LDS: Kbuf[0], Kbuf[1], Vbuf[0], Vbuf[1]; rows unpadded, 16-byte chunks
     // XOR-swizzled per row (see swk / swv) so that the MFMA operand reads are
     // free of bank conflicts.
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];
+    // Q enters through LDS as well (see below) where the extra LDS still
+    // leaves the workgroup's occupancy unchanged: not for d = 128 with four
+    // waves, whose two workgroups per CU already take 128 KB.
+    constexpr bool QLDS = D == 64;
+    constexpr int QST = QLDS ? NW * 32 * RB : 0;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE + QST];
 
     const int B = a.B, H = a.H, N = a.N;
     const int nq = (N + BM - 1) / BM;
@@ -105,13 +110,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     const int myq = qw + l32;             // query row owned by this lane
 
     // Q^T fragments (B operand): lane holds Q[myq][c*16 + hi*8 .. +8].
+    // With QLDS each wave first copies its 32 rows into its own LDS region
+    // by direct-to-LDS loads of whole 16-byte row chunks (chunks XOR-
+    // swizzled by row; rows past N clamped to N - 1), and the fragments are
+    // read from there after the prologue's barrier; otherwise each lane
+    // loads its own row.
     bf16x8 qf[DC];
+    unsigned char* qst = smem + 4 * TILE + wave * 32 * RB;
+    auto qdma = [&] {
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (myq < N) v = ld16(Qg + (size_t)myq * rs + c * 16 + hi * 8);
-        v ^= a.qsign;
-        qf[c] = as_bf16x8(v);
+        for (int j = 0; j < 32 * CPR / 64; ++j) {
+            const int i = j * 64 + lane;
+            const int row = i / CPR, pc = i % CPR;
+            const int grow = min(qw + row, N - 1);
+            __builtin_amdgcn_global_load_lds(Qg + (size_t)grow * rs + ((pc ^ (row & (CPR - 1))) << 3),
+                                             (lds_void_t*)(qst + j * 1024), 16, 0, 0);
+        }
+    };
+    if constexpr (QLDS) {
+        qdma();
+    } else {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (myq < N) v = ld16(Qg + (size_t)myq * rs + c * 16 + hi * 8);
+            v ^= a.qsign;
+            qf[c] = as_bf16x8(v);
+        }
     }
 
     const int kend = CAUSAL ? min(N, q0 + BM) : N;
@@ -364,6 +389,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     if (ntiles > 1) dma(Kg, 1, 1, false);
     wait_dma();
     __syncthreads();
+    if constexpr (QLDS) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(qst + l32 * RB + (((2 * c + hi) ^ (l32 & (CPR - 1))) << 4));
+            if (myq >= N) v = u32x4{0u, 0u, 0u, 0u};
+            v ^= a.qsign;
+            qf[c] = as_bf16x8(v);
+        }
+    }
     f32x16 sa[KB], sb[KB];
     scores(sa, kbuf(0));
     __syncthreads();   // Kbuf[0] receives K_2 in iteration 0
@@ -407,23 +441,34 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     }
 
     // Epilogue: O = O^T / l (rounded to bf16), LSE = ln-domain m + ln l.
+    // O leaves through LDS: each wave stages its 32 rows in its own part of
+    // the K/V buffers (idle since the last barrier), 16-byte chunks of a row
+    // XOR-swizzled by the row, then writes whole 16-byte chunks of rows, so
+    // that the global stores cover contiguous rows instead of 8 bytes of 32
+    // rows per instruction.
     const float lt = sum_halves(l);
     const float inv = 1.0f / lt;
-    if (myq < N) {
-        __bf16* orow = Og + (size_t)myq * rs;
+    static_assert(NW * 32 * RB <= 4 * TILE, "O staging fits the K/V buffers");
+    unsigned char* ow = smem + wave * 32 * RB;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = db * 32 + 8 * g + 4 * hi;
-                u32x2 w;
-                w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-                w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-                st8(orow + d0, w);
-            }
+        for (int g = 0; g < 4; ++g) {
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+            w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+            // Elements d0 .. d0 + 3, d0 = db*32 + 8g + 4hi: chunk db*4 + g, bytes 8hi .. 8hi + 7.
+            *reinterpret_cast<u32x2*>(ow + l32 * RB + (((db * 4 + g) ^ (l32 & (CPR - 1))) << 4) + 8 * hi) = w;
         }
-        if (hi == 0) a.lse[(size_t)bh * N + myq] = (m + __builtin_log2f(lt)) * kLn2;
     }
+#pragma unroll
+    for (int j = 0; j < 32 * CPR / 64; ++j) {
+        const int i = j * 64 + lane;
+        const int row = i / CPR, ch = i % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ow + row * RB + ((ch ^ (row & (CPR - 1))) << 4));
+        if (qw + row < N) st16(Og + (size_t)(qw + row) * rs + ch * 8, v);
+    }
+    if (myq < N && hi == 0) a.lse[(size_t)bh * N + myq] = (m + __builtin_log2f(lt)) * kLn2;
 }
 
 template <int D, bool CAUSAL>
