@@ -32,22 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 
 
-CSRC = os.path.join(ROOT, "exact_tiled_attention_13_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-
-
-def kernel_source_hash(name: str) -> str:
-    """sha256 over the sources and build script a kernel is compiled from; the
-    HBM byte counts stored in profiles/ are used only while this matches."""
-    import hashlib
-
-    main = "fwd_bf16.hip" if name.startswith("fwd") else "bwd_bf16.hip"
-    h = hashlib.sha256()
-    for f in [os.path.join(CSRC, x) for x in ("common.hpp", "lds_tile.hpp", "kernels.hpp", main)] + [
-            os.path.join(ROOT, "exact_tiled_attention_13_amd", "build.py")]:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
 
 
 def measured_traffic(name: str):
@@ -59,6 +44,8 @@ def measured_traffic(name: str):
             entry = json.load(f)["kernels"].get(name)
     except (OSError, ValueError, KeyError):
         return None
+    from exact_tiled_attention_13_amd.traffic import kernel_source_hash
+
     if not entry or entry.get("source_sha256") != kernel_source_hash(name):
         return None
     return float(entry["hbm_bytes"])
@@ -110,24 +97,38 @@ def _raw(name, *args):
     return lambda: fn(*args)
 
 
-def _time_calls(f, reps, warmup):
-    """Mean ms of `reps` back-to-back calls of f (returning a library status) between two HIP events on the
-    current stream, after `warmup` untimed calls."""
+def _time_calls(f, reps, warmup, min_warm_ms=20.0, min_timed_ms=50.0):
+    """Mean ms of back-to-back calls of f (returning a library status) between two HIP events on the
+    current stream. Short calls are repeated until the untimed warm-up covers at least min_warm_ms and the
+    timed loop at least min_timed_ms of GPU time (and at least `warmup` / `reps` calls): a loop of ten
+    0.1 ms calls straight after the host has been preparing inputs runs partly before the GPU's clocks have
+    come back up and reads up to 20% slow."""
+    import math
+
     import torch
 
-    for _ in range(warmup):
-        if f() != 0:
-            raise RuntimeError("library call failed during warmup")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    bad = 0
-    e0.record()
-    for _ in range(reps):
-        bad |= f()
-    e1.record()
-    torch.cuda.synchronize()
+    def run(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bad = 0
+        e0.record()
+        for _ in range(n):
+            bad |= f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), bad
+
+    t, bad = run(warmup)
+    if bad:
+        raise RuntimeError("library call failed during warmup")
+    est = max(t / max(warmup, 1), 1e-3)
+    t, bad = run(max(0, math.ceil(min_warm_ms / est) - warmup))
+    if bad:
+        raise RuntimeError("library call failed during warmup")
+    n = max(reps, math.ceil(min_timed_ms / est))
+    t, bad = run(n)
     if bad:
         raise RuntimeError("library call failed in the timed loop")
-    return e0.elapsed_time(e1) / reps
+    return t / n
 
 
 def time_passes(w, reps=10, warmup=3):

@@ -11,7 +11,8 @@ N(0, 1) drawn on the GPU from a fixed seed and rounded to bf16 (timing only;
 parity at these shapes is the tests' job). Each pass is timed with HIP events
 around R back-to-back calls of the library's C entry points (forward:
 attn_fwd; backward: attn_bwd, i.e. preprocess + dK/dV + dQ, from the
-forward's O and LSE), after two untimed calls. Counted FLOP as everywhere
+forward's O and LSE), repeated until the timed loop covers at least 50 ms
+after at least 20 ms of untimed calls. Counted FLOP as everywhere
 else: forward 4*B*H*N^2*d, backward 2.5x that, both halved under the causal
 mask. Prints one JSON object per point and a markdown table.
 """
@@ -33,22 +34,29 @@ SEQ = (512, 1024, 2048, 4096, 8192, 16384)
 HEADS = ((32, 64), (16, 128))
 
 
-def _time(f, reps: int) -> float:
+def _time(f, reps: int, min_warm_ms: float = 20.0, min_timed_ms: float = 50.0) -> float:
+    """Mean ms per call over at least `reps` calls and min_timed_ms of GPU time,
+    after at least min_warm_ms of untimed calls (so the clocks are up)."""
+    import math
+
     import torch
 
-    for _ in range(2):
-        if f() != 0:
-            raise RuntimeError("library call failed during warmup")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    bad = 0
-    e0.record()
-    for _ in range(reps):
-        bad |= f()
-    e1.record()
-    torch.cuda.synchronize()
-    if bad:
-        raise RuntimeError("library call failed in the timed loop")
-    return e0.elapsed_time(e1) / reps
+    def run(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bad = 0
+        e0.record()
+        for _ in range(n):
+            bad |= f()
+        e1.record()
+        torch.cuda.synchronize()
+        if bad:
+            raise RuntimeError("library call failed")
+        return e0.elapsed_time(e1)
+
+    est = max(run(2) / 2, 1e-3)
+    run(max(0, math.ceil(min_warm_ms / est) - 2))
+    n = max(reps, math.ceil(min_timed_ms / est))
+    return run(n) / n
 
 
 def main():
