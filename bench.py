@@ -299,8 +299,10 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    kern_ms = {n: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
-               for i, n in enumerate(names)}
+    launch_ms = {n: sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+                 for i, n in enumerate(names)}
+    kern_ms = {n: sum(v) / len(v) for n, v in launch_ms.items()}
+    kern_med = {n: (v[(len(v) - 1) // 2] + v[len(v) // 2]) / 2 for n, v in launch_ms.items()}
 
     # Algorithmic work per launch.
     work = {}
@@ -323,6 +325,9 @@ def main():
         else:
             breakdown[n] = {"ms": round(kern_ms[n], 4), "gbs": round(rate / 1e9, 1),
                             "frac_hbm_peak": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
+        # Mean (above), median and minimum over the timed steps' launches.
+        breakdown[n]["ms_median"] = round(kern_med[n], 4)
+        breakdown[n]["ms_min"] = round(launch_ms[n][0], 4)
     passes = {}
     for c in masks:
         tag = "causal" if c else "noncausal"
