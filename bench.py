@@ -73,7 +73,14 @@ def cpu_baseline(q, k, v, do, scale, heads=2):
             attn_bwd_head(qh, kh, vh, gh, causal, scale)
             flops += 3.5 * counted_fwd(1, 1, N, d, causal)
     t1 = time.perf_counter()
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {
         "value": flops / (t1 - t0) / 1e12,
         "unit": "TFLOP/s",
@@ -83,6 +90,9 @@ def cpu_baseline(q, k, v, do, scale, heads=2):
                    f"for {heads} of the {H} heads of the same inputs, {t1 - t0:.1f} s; value uses the "
                    f"same counted-FLOP formula as the GPU step"),
         "seconds": round(t1 - t0, 2),
+        "cpu_model": cpu,
+        "blas": ", ".join(f"{i.get('internal_api', '?')} {i.get('version', '')} ({i.get('num_threads', 1)} threads)"
+                          for i in blas) or "none found",
     }
 
 
