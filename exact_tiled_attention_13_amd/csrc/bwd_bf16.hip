@@ -68,6 +68,45 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Output rows through LDS. In a 32x32 accumulator whose columns are 32 rows
+// of an output (lane % 32) and whose rows are d (block db), lane (l32, hi)
+// holds elements db*32 + 8g + 4hi .. +3 of row l32 for g = 0..3.
+// stage_rows packs them (times sc) to bf16 and writes them to a 32-row LDS
+// region, 16-byte chunks of a row XOR-swizzled by the row; store_rows reads
+// back whole 16-byte chunks and writes rows r0 .. r0+31 (those below n) of
+// g (row stride rs elements), so that each store instruction covers
+// contiguous rows instead of 8 bytes of 32 rows. The region belongs to one
+// wave; LDS operations of a wave run in order, so no barrier is needed
+// between the two.
+template <int D>
+__device__ __forceinline__ void stage_rows(unsigned char* sw, const f32x16 (&acc)[D / 32], float sc, int l32,
+                                           int hi) {
+    constexpr int RB = D * 2, CPR = RB / 16;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc);
+            w[1] = pack_bf16x2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
+            *reinterpret_cast<u32x2*>(sw + l32 * RB + (((db * 4 + g) ^ (l32 & (CPR - 1))) << 4) + 8 * hi) = w;
+        }
+}
+
+template <int D>
+__device__ __forceinline__ void store_rows(__bf16* g, size_t rs, const unsigned char* sw, int r0, int n,
+                                           int lane) {
+    constexpr int RB = D * 2, CPR = RB / 16;
+#pragma unroll
+    for (int j = 0; j < 32 * CPR / 64; ++j) {
+        const int i = j * 64 + lane;
+        const int row = i / CPR, ch = i % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sw + row * RB + ((ch ^ (row & (CPR - 1))) << 4));
+        if (r0 + row < n) st16(g + (size_t)(r0 + row) * rs + ch * 8, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dK, dV for d = 64: one workgroup of 4 waves per 128 keys (32 per wave, K
 // and V rows in VGPRs; two workgroups share a CU), looping over query tiles
 // of 64 rows staged in LDS by direct loads.
@@ -371,24 +410,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
         return;
     }
-    if (myk < N) {
-        __bf16* dkrow = static_cast<__bf16*>(a.dk) + kvbase + (size_t)myk * rskv;
-        __bf16* dvrow = static_cast<__bf16*>(a.dv) + kvbase + (size_t)myk * rskv;
-        const float sc = a.scale;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = db * 32 + 8 * g + 4 * hi;
-                u32x2 wk, wv;
-                wk[0] = pack_bf16x2(dkacc[db][4 * g] * sc, dkacc[db][4 * g + 1] * sc);
-                wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * sc, dkacc[db][4 * g + 3] * sc);
-                wv[0] = pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]);
-                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
-                st8(dkrow + d0, wk);
-                st8(dvrow + d0, wv);
-            }
-    }
+    // dK, then dV, leave through LDS (this wave's part of the tile stages,
+    // idle since the last barrier) as whole 16-byte chunks of key rows.
+    static_assert(NW * 32 * RB <= 2 * STAGE, "dK/dV staging fits the tile stages");
+    unsigned char* sw = smem + wave * 32 * RB;
+    stage_rows<D>(sw, dkacc, a.scale, l32, hi);
+    store_rows<D>(static_cast<__bf16*>(a.dk) + kvbase, rskv, sw, kw, N, lane);
+    stage_rows<D>(sw, dvacc, 1.0f, l32, hi);
+    store_rows<D>(static_cast<__bf16*>(a.dv) + kvbase, rskv, sw, kw, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -772,20 +801,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         }
         return;
     }
-    if (myk < N) {
-        __bf16* row = static_cast<__bf16*>(pwave ? a.dv : a.dk) + kvbase + (size_t)myk * rskv;
-        const float sc = pwave ? 1.0f : a.scale;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = db * 32 + 8 * g + 4 * hi;
-                u32x2 w;
-                w[0] = pack_bf16x2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc);
-                w[1] = pack_bf16x2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
-                st8(row + d0, w);
-            }
-    }
+    // dV (P wave) or dK (dS wave) leaves through LDS as whole 16-byte chunks
+    // of key rows, once every wave is past its last LDS read (the dS wave's
+    // final step above).
+    __syncthreads();
+    static_assert(NW * 32 * RB <= LDS_BYTES, "dK/dV staging fits the LDS");
+    unsigned char* sw = smem + wave * 32 * RB;
+    stage_rows<D>(sw, acc, pwave ? 1.0f : a.scale, l32, hi);
+    store_rows<D>(static_cast<__bf16*>(pwave ? a.dv : a.dk) + kvbase, rskv, sw, kw, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -958,19 +981,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
         __syncthreads();
     }
 
-    if (myq < N) {
-        __bf16* row = static_cast<__bf16*>(a.dq) + base + (size_t)myq * rs;
-        const float sc = a.scale;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = pack_bf16x2(dqacc[db][4 * g] * sc, dqacc[db][4 * g + 1] * sc);
-                w[1] = pack_bf16x2(dqacc[db][4 * g + 2] * sc, dqacc[db][4 * g + 3] * sc);
-                st8(row + db * 32 + 8 * g + 4 * hi, w);
-            }
-    }
+    // dQ leaves through LDS (this wave's part of the K/V buffers, idle since
+    // the last barrier) as whole 16-byte chunks of rows.
+    static_assert(NW * 32 * RB <= 4 * T::BYTES, "dQ staging fits the K/V buffers");
+    unsigned char* sw = smem + wave * 32 * RB;
+    stage_rows<D>(sw, dqacc, a.scale, l32, hi);
+    store_rows<D>(static_cast<__bf16*>(a.dq) + base, rs, sw, qw, N, lane);
 }
 
 // Split grouped-query dK/dV: sums the gsplit fp32 partials of each element in
