@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     FA_ERR_WORKSPACE,
     FA_OK,
     LIB_PATH,
+    LIB_POISON_PATH,
     FaError,
     attn_bwd,
     attn_bwd_dkdv,
@@ -31,6 +32,7 @@ from ._binding import (  # noqa: F401
     default_scale,
     lib,
     status_string,
+    use_library,
     workspace,
     workspace_gqa,
 )

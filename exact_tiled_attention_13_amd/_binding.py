@@ -8,6 +8,7 @@ rejected, an exception is raised.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -15,7 +16,12 @@ import threading
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
+_PKG = os.path.dirname(os.path.abspath(__file__))
+# The attention library. FA_MI355X_LIB may name another build of the same
+# sources instead (for instance libfa_mi355x_ldspoison.so, the race-check
+# build whose kernels fill their LDS with NaN before use).
+LIB_PATH = os.environ.get("FA_MI355X_LIB") or os.path.join(_PKG, "libfa_mi355x.so")
+LIB_POISON_PATH = os.path.join(_PKG, "libfa_mi355x_ldspoison.so")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = 1
@@ -45,42 +51,62 @@ def lib() -> ctypes.CDLL:
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB_PATH):
-                raise RuntimeError(
-                    f"{LIB_PATH} is missing: build it with `python -m exact_tiled_attention_13_amd.build` "
-                    "(or __graft_entry__.build()); there is no fallback path")
-            L = ctypes.CDLL(LIB_PATH)
-            vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-            L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
-            L.attn_fwd.restype = ci
-            L.attn_fwd_fp32.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
-            L.attn_fwd_fp32.restype = ci
-            L.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci]
-            L.attn_bwd_workspace_size.restype = sz
-            L.attn_bwd.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, cf, vp]
-            L.attn_bwd.restype = ci
-            L.attn_bwd_prep.argtypes = [vp, vp, vp, vp, sz, ci, ci, ci, ci, vp]
-            L.attn_bwd_prep.restype = ci
-            L.attn_bwd_dkdv.argtypes = [vp] * 5 + [sz, vp, vp, ci, ci, ci, ci, ci, cf, vp]
-            L.attn_bwd_dkdv.restype = ci
-            L.attn_bwd_dq.argtypes = [vp] * 5 + [sz, vp, ci, ci, ci, ci, ci, cf, vp]
-            L.attn_bwd_dq.restype = ci
-            L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
-            L.attn_fwd_gqa.restype = ci
-            L.attn_bwd_gqa.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, ci, cf, vp]
-            L.attn_bwd_gqa.restype = ci
-            L.attn_bwd_gqa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
-            L.attn_bwd_gqa_workspace_size.restype = sz
-            L.attn_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
-            L.attn_decode_workspace_size.restype = sz
-            L.attn_decode.argtypes = [vp] * 5 + [vp, sz] + [ci, ci, ci, ci, ci, ci, ci, cf, vp]
-            L.attn_decode.restype = ci
-            L.attn_fwd_fp8.argtypes = [vp, vp, vp, ci, cf, cf, cf, vp, vp, ci, ci, ci, ci, ci, cf, vp]
-            L.attn_fwd_fp8.restype = ci
-            L.fa_status_string.argtypes = [ci]
-            L.fa_status_string.restype = ctypes.c_char_p
-            _lib = L
+            _lib = _load(LIB_PATH)
         return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Route every call of this module to the library at `path` (another build of the same sources, e.g.
+    LIB_POISON_PATH) until the block exits."""
+    global _lib
+    alt = _load(path)
+    with _lock:
+        prev = _lib
+        _lib = alt
+    try:
+        yield alt
+    finally:
+        with _lock:
+            _lib = prev
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_tiled_attention_13_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(path)
+    vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_fwd.restype = ci
+    L.attn_fwd_fp32.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_fwd_fp32.restype = ci
+    L.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci]
+    L.attn_bwd_workspace_size.restype = sz
+    L.attn_bwd.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, cf, vp]
+    L.attn_bwd.restype = ci
+    L.attn_bwd_prep.argtypes = [vp, vp, vp, vp, sz, ci, ci, ci, ci, vp]
+    L.attn_bwd_prep.restype = ci
+    L.attn_bwd_dkdv.argtypes = [vp] * 5 + [sz, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_bwd_dkdv.restype = ci
+    L.attn_bwd_dq.argtypes = [vp] * 5 + [sz, vp, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_bwd_dq.restype = ci
+    L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_fwd_gqa.restype = ci
+    L.attn_bwd_gqa.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_bwd_gqa.restype = ci
+    L.attn_bwd_gqa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.attn_bwd_gqa_workspace_size.restype = sz
+    L.attn_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.attn_decode_workspace_size.restype = sz
+    L.attn_decode.argtypes = [vp] * 5 + [vp, sz] + [ci, ci, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_decode.restype = ci
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, ci, cf, cf, cf, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_fwd_fp8.restype = ci
+    L.fa_status_string.argtypes = [ci]
+    L.fa_status_string.restype = ctypes.c_char_p
+    return L
 
 
 def status_string(status: int) -> str:

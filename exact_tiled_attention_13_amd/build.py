@@ -1,8 +1,17 @@
-"""Build libfa_mi355x.so in-tree with hipcc, for gfx950 only.
+"""Build the package's shared libraries in-tree with hipcc, for gfx950 only.
 
 Usage: ``python -m exact_tiled_attention_13_amd.build`` (or call :func:`build`).
+
+* ``libfa_mi355x.so`` -- the attention library (include/fa_mi355x.h);
+* ``libfa_mi355x_ldspoison.so`` -- the same sources built with
+  ``-DFA_LDS_POISON``: every kernel fills its LDS with NaN bit patterns
+  before its first barrier, so that a read of LDS that no load or store
+  wrote shows up as NaN in the results (a race check for the parity tests);
+* ``libfa_micro.so`` -- microbenchmarks of the units the kernels depend on
+  (include/fa_micro.h).
+
 Each source compiles to an object under ``_build/`` in parallel, then one
-``hipcc -shared`` link writes ``exact_tiled_attention_13_amd/libfa_mi355x.so``.
+``hipcc -shared`` link per library writes it into the package directory.
 """
 
 from __future__ import annotations
@@ -17,8 +26,18 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa_mi355x.so")
+LIB_POISON = os.path.join(PKG, "libfa_mi355x_ldspoison.so")
+LIB_MICRO = os.path.join(PKG, "libfa_micro.so")
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_fp32.hip", "fwd_fp8.hip", "bwd_bf16.hip", "decode_bf16.hip"]
+MICRO_SOURCES = ["micro.hip"]
+
+# (library, sources, extra defines, object-name suffix)
+TARGETS = [
+    (LIB, SOURCES, (), ""),
+    (LIB_POISON, SOURCES, ("-DFA_LDS_POISON=1",), "_ldspoison"),
+    (LIB_MICRO, MICRO_SOURCES, (), ""),
+]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -43,9 +62,11 @@ EXTRA_FLAGS = {"bwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
                "fwd_fp8.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, defines, suffix = job
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + suffix + ".o")
+    cmd = [HIPCC, *FLAGS, *defines, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o",
+           obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -66,20 +87,26 @@ def _check_stubs(lib: str) -> None:
         raise RuntimeError("kernel launch stubs missing from the host code:\n" + "\n".join(missing))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library. Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     _check_stubs(tmp)
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source of every library and link them. Returns the attention library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(src, defines, suffix) for _, srcs, defines, suffix in TARGETS for src in srcs]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = dict(zip(jobs, ex.map(_compile, jobs)))
+    for lib, srcs, defines, suffix in TARGETS:
+        _link(lib, [objs[(src, defines, suffix)] for src in srcs])
+        if verbose:
+            print(f"built {lib}")
     return LIB
 
 

@@ -98,6 +98,24 @@ struct DecodeArgs {
     uint32_t qsign;   // as in FwdArgs
 };
 
+// Race check. In the build with -DFA_LDS_POISON=1 every kernel calls this on
+// each of its LDS arrays before anything else: the workgroup fills the array
+// with 0xFF bytes (a NaN in fp32 and in bf16) and waits at a barrier, so a
+// read of LDS that none of the kernel's loads or stores wrote carries NaN
+// into the results (even a probability of zero times NaN is NaN). In the
+// normal build it compiles to nothing. `bytes` is a multiple of 4 and `p` is
+// 4-byte aligned.
+__device__ __forceinline__ void lds_poison(void* p, int bytes) {
+#if defined(FA_LDS_POISON) && FA_LDS_POISON
+    uint32_t* w = static_cast<uint32_t*>(p);
+    for (int i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0xFFFFFFFFu;
+    __syncthreads();
+#else
+    (void)p;
+    (void)bytes;
+#endif
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Remap the dispatch index so that XCD x receives a contiguous range of
 // logical tile indices: the query blocks of one head then run on one XCD at

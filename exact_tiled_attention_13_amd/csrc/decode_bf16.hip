@@ -48,6 +48,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     constexpr int kVmcntNL = vmcnt_only(NL);
     constexpr int kVmcnt2NL = vmcnt_only(2 * NL);
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * 2 * T::BYTES];
+    lds_poison(smem, sizeof(smem));
 
     const int S = a.S, H = a.H, Hkv = a.Hkv, Nq = a.Nq, Nk = a.Nk, R = a.R;
     const int bh = blockIdx.x / S;
@@ -243,6 +244,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     constexpr int SG = 256 / TPR;        // chunk groups
     __shared__ f32x4 part[SG][TPR];
     __shared__ float red[4];
+    lds_poison(part, sizeof(part));
+    lds_poison(red, sizeof(red));
     const int t = threadIdx.x;
     const long long row = blockIdx.x;    // (b, i, h)
     const int h = (int)(row % a.H);

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     constexpr bool QLDS = D == 64;
     constexpr int QST = QLDS ? NW * 32 * RB : 0;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE + QST];
+    lds_poison(smem, sizeof(smem));
 
     const int B = a.B, H = a.H, N = a.N;
     const int nq = (N + BM - 1) / BM;

@@ -23,6 +23,8 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdArgs a) {
     constexpr int DB = D / 32;
     __shared__ float Ks[BN * KS];
     __shared__ __attribute__((aligned(16))) float Vs[BN * VS];
+    lds_poison(Ks, sizeof(Ks));
+    lds_poison(Vs, sizeof(Vs));
 
     const int B = a.B, H = a.H, N = a.N;
     const int nq = (N + BM - 1) / BM;
