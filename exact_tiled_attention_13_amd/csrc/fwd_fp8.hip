@@ -70,6 +70,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(Fp8Args a) {
     static_assert(D == 128, "the FP8 forward is written for d = 128");
     static_assert(IPW * NW == NINST, "tile loads must split evenly over the waves");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];   // K[2], V^T[2]
+    lds_poison(smem, sizeof(smem));
 
     const int B = a.B, H = a.H, N = a.N;
     const int nq = (N + BM - 1) / BM;
@@ -260,6 +261,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(Fp8Args a) {
         for (int db = 0; db < DB; ++db)
             va[db] = join(*reinterpret_cast<const u32x4*>(Vs + voff(db, 0)),
                           *reinterpret_cast<const u32x4*>(Vs + voff(db, 1)));
+        if constexpr (decltype(masked_c)::value) {
+            // Ragged last tile: byte j of this lane's 32 V^T bytes is key t*BN + 32*hi + j; bytes of keys
+            // at or past N are the caller's padding. Their P is 0, but 0 times a NaN code is NaN, so they
+            // are cleared in registers and the result does not depend on what the padding holds.
+            const int valid = N - (t * BN + 32 * hi);
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const int nb = valid - 4 * w;   // real bytes in dword w
+                const uint32_t keep = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - nb))));
+#pragma unroll
+                for (int db = 0; db < DB; ++db) va[db][w] = (int)((uint32_t)va[db][w] & keep);
+            }
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] = mfma_fp8(va[db], pb, oacc[db]);
         fence();

@@ -189,7 +189,8 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, con
  *   q8, k8   E4M3 bytes, [B, N, H, d], device, read-only.
  *   vt8      V transposed per head, E4M3 bytes, [B, H, d, ldv]: row (b, h, c)
  *            holds V[b, :, h, c] for keys 0 .. N-1 contiguously; bytes N ..
- *            ldv-1 of each row are read and must hold finite values (zero).
+ *            ldv-1 of each row are padding: read, but cleared before use, so
+ *            they may hold anything (NaN codes included).
  *   ldv      bytes per vt8 row: a multiple of 16 and at least 64 * ceil(N/64).
  *   q_descale, k_descale, v_descale: per-tensor factors, finite and > 0; the
  *            real inputs are value * descale.
