@@ -35,35 +35,50 @@ namespace fa {
 // -D_i = -sum_c dO[b,i,h,c] * O[b,i,h,c] and LSE_i * log2(e), fp32 [B, H, Npad].
 // D is stored negated so that the dK/dV kernel can start its dP accumulator
 // at -D (dP - D then comes out of the MFMAs) and the dQ kernel adds it.
+// One workgroup per 64-row block of one head: D/8 threads reduce a row (16
+// bytes of O and dO each), the row results gather in LDS, and each statistic
+// leaves as one contiguous 256-byte run (rows of one head are contiguous in
+// the [B, H, Npad] arrays; per-row 4-byte stores strided by Npad would write
+// whole memory sectors for 4 bytes each).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     constexpr int TPR = D / 8;               // threads per row (8 elements each)
-    constexpr int RPB = 256 / TPR;           // rows per block
+    constexpr int RPP = 256 / TPR;           // rows per pass
+    constexpr int ROWS = 64;                 // rows per workgroup
+    __shared__ float dsh[ROWS];
+    lds_poison(dsh, sizeof(dsh));
     const int npad = (a.N + 63) & ~63;
-    const long long rows = (long long)a.B * npad * a.H;
-    const long long r = (long long)blockIdx.x * RPB + threadIdx.x / TPR;   // (b, n, h), n < npad
+    const int nblk = npad / ROWS;
+    const int blk = blockIdx.x % nblk;
+    const int bh = blockIdx.x / nblk;        // b * H + h
+    const int b = bh / a.H, h = bh - b * a.H;
     const int c = threadIdx.x % TPR;
-    const long long h = r % a.H;
-    const long long n = (r / a.H) % npad;
-    const long long b = r / ((long long)a.H * npad);
-    const bool real = r < rows && n < a.N;
-    float acc = 0.f;
-    if (real) {
-        const long long src = ((b * a.N + n) * a.H + h) * D + c * 8;
-        const u32x4 o = ld16(static_cast<const __bf16*>(a.o) + src);
-        const u32x4 g = ld16(static_cast<const __bf16*>(a.dO) + src);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            acc += __uint_as_float(o[w] << 16) * __uint_as_float(g[w] << 16);
-            acc += __uint_as_float(o[w] & 0xffff0000u) * __uint_as_float(g[w] & 0xffff0000u);
+    for (int p = 0; p < ROWS / RPP; ++p) {
+        const int rl = p * RPP + threadIdx.x / TPR;
+        const int n = blk * ROWS + rl;
+        float acc = 0.f;
+        if (n < a.N) {
+            const size_t src = (((size_t)b * a.N + n) * a.H + h) * D + c * 8;
+            const u32x4 o = ld16(static_cast<const __bf16*>(a.o) + src);
+            const u32x4 g = ld16(static_cast<const __bf16*>(a.dO) + src);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc += __uint_as_float(o[w] << 16) * __uint_as_float(g[w] << 16);
+                acc += __uint_as_float(o[w] & 0xffff0000u) * __uint_as_float(g[w] & 0xffff0000u);
+            }
         }
-    }
 #pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (r < rows && c == 0) {
-        const long long i = (b * a.H + h) * npad + n;
-        a.dd[i] = real ? -acc : 0.f;
-        a.lse2[i] = real ? a.lse[(b * a.H + h) * a.N + n] * kLog2e : INFINITY;
+        for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        if (c == 0) dsh[rl] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < ROWS) {
+        const int n = blk * ROWS + threadIdx.x;
+        const size_t i = (size_t)bh * npad + n;
+        const bool real = n < a.N;
+        a.dd[i] = real ? -dsh[threadIdx.x] : 0.f;
+        a.lse2[i] = real ? a.lse[(size_t)bh * a.N + n] * kLog2e : INFINITY;
     }
 }
 
@@ -128,6 +143,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int STAGE = 2 * T::BYTES + 2 * BQ * 4;   // Q, dO, lse2, dd
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+    lds_poison(smem, sizeof(smem));
 
     const int B = a.B, H = a.H, N = a.N;
     const int npad = (N + 63) & ~63;
@@ -466,6 +482,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     constexpr int LDS_BYTES = POFF + 2 * PXB;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+    lds_poison(smem, sizeof(smem));
 
     const int B = a.B, H = a.H, N = a.N;
     const int npad = (N + 63) & ~63;
@@ -828,6 +845,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     constexpr int RB = T::RB;
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * T::BYTES];   // Kbuf[2], Vbuf[2]
+    lds_poison(smem, sizeof(smem));
 
     const int B = a.B, H = a.H, N = a.N;
     const int npad = (N + 63) & ~63;
@@ -1019,9 +1037,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a) {
 
 template <int D>
 static hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
-    const long long rows = (long long)a.B * ((a.N + 63) & ~63) * a.H;
-    const long long rpb = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, a);
+    const long long blocks = (long long)a.B * a.H * (((a.N + 63) & ~63) / 64);
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -9,7 +9,10 @@
 
 #include <algorithm>
 #include <functional>
+#include <map>
+#include <mutex>
 #include <queue>
+#include <tuple>
 #include <vector>
 
 #include "common.hpp"
@@ -58,7 +61,7 @@ inline int decode_chunks(int B, int Hkv, int Nk, int* L) {
 // per tile at d = 128, 1 us at d = 64), and a split adds its partial sums'
 // HBM traffic at 4 TB/s. A larger S must win by 3%. Grids of at least four
 // workgroups per slot are left unsplit.
-inline int dkdv_gqa_splits(int B, int H, int Hkv, int N, int d, bool causal) {
+inline int dkdv_gqa_splits_uncached(int B, int H, int Hkv, int N, int d, bool causal) {
     const int G = H / Hkv;
     if (G <= 1) return 1;
     const long long nk = (N + 127) / 128;
@@ -98,6 +101,26 @@ inline int dkdv_gqa_splits(int B, int H, int Hkv, int N, int d, bool causal) {
         }
     }
     return best_s;
+}
+
+// dkdv_gqa_splits_uncached memoised per shape: the simulation walks up to
+// 16384 workgroups per candidate, which a caller repeating one shape (every
+// training step) should not pay on each call. The table only grows with the
+// number of distinct shapes a process uses; a mutex guards it.
+inline int dkdv_gqa_splits(int B, int H, int Hkv, int N, int d, bool causal) {
+    if (H / Hkv <= 1) return 1;
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, int, int, bool>, int> memo;
+    const auto key = std::make_tuple(B, H, Hkv, N, d, causal);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = memo.find(key);
+        if (it != memo.end()) return it->second;
+    }
+    const int s = dkdv_gqa_splits_uncached(B, H, Hkv, N, d, causal);
+    std::lock_guard<std::mutex> lock(mu);
+    memo.emplace(key, s);
+    return s;
 }
 
 }  // namespace fa

@@ -55,8 +55,6 @@ from .attn_ref import (  # noqa: F401
     attn_fwd_rows,
     attn_bwd,
     attn_bwd_head,
-    flops_fwd,
-    flops_bwd,
 )
 from .gqa import attn_bwd_gqa, attn_fwd_gqa  # noqa: F401
 from .decode import attn_decode, attn_decode_split, attn_partial, bytes_decode, merge_partials  # noqa: F401

@@ -55,17 +55,6 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def flops_fwd(B: int, H: int, N: int, d: int, causal: bool) -> float:
-    """Counted forward FLOP: the two N x N x d products, 4*B*H*N^2*d, halved under causal."""
-    f = 4.0 * B * H * N * N * d
-    return f / 2 if causal else f
-
-
-def flops_bwd(B: int, H: int, N: int, d: int, causal: bool) -> float:
-    """Counted backward FLOP: 2.5x the forward count (five N x N x d products)."""
-    return 2.5 * flops_fwd(B, H, N, d, causal)
-
-
 def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, scale: float):
     """Scaled, masked scores of the given query rows against all keys: [len(rows), N]."""
     s = scale * (q_rows @ k.T)

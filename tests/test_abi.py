@@ -1,7 +1,11 @@
-"""C-ABI checks that need no GPU: the library loads, exports every entry point
-declared in include/fa_mi355x.h, and rejects bad arguments before any HIP call.
+"""C-ABI checks that need no GPU: the libraries load, export every entry point
+declared in include/fa_mi355x.h and include/fa_micro.h, and reject bad
+arguments before any HIP call.
 
-Every call made here fails validation, so no kernel is launched.
+Every call made here fails validation, so no kernel is launched. The calls
+pass fake device addresses, so they run only on a host without a GPU (no
+/dev/kfd): there, even a validation check that regressed could not launch a
+kernel on those addresses; on a GPU host they are skipped.
 """
 
 import ctypes
@@ -18,6 +22,9 @@ HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
 # Fake device addresses: non-null and 16-byte aligned (never dereferenced).
 P = 0x100000
 MIS = 0x100008  # 8-byte aligned only
+
+no_gpu_only = pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                                 reason="fake device addresses are passed only where no GPU exists")
 
 
 def declared_functions():
@@ -36,6 +43,35 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_poison_build_exports_every_declared_symbol():
+    L = ctypes.CDLL(fa.LIB_POISON_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_micro_library_exports_every_declared_symbol():
+    from exact_tiled_attention_13_amd import micro
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fa_micro.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", text, flags=re.M)))
+    assert names == ["fa_micro_atomic_add", "fa_micro_exp2", "fa_micro_fp8_dot", "fa_micro_mfma_bf16"]
+    L = ctypes.CDLL(micro.LIB_MICRO)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+@no_gpu_only
+def test_micro_rejects_bad_arguments():
+    from exact_tiled_attention_13_amd import micro
+    L = micro.lib()
+    assert L.fa_micro_mfma_bf16(0, P, 4, 2, 0, None) == 1
+    assert L.fa_micro_mfma_bf16(P, P, 4, 3, 0, None) == 1       # odd iteration count
+    assert L.fa_micro_mfma_bf16(P, P, 4, 2, 3, None) == 1       # unknown operand mode
+    assert L.fa_micro_exp2(P, P, 0, 1, None) == 1
+    assert L.fa_micro_fp8_dot(P, P, P, 1, 65, None) == 1
+    assert L.fa_micro_fp8_dot(P, MIS, P, 1, 1, None) == 1
+    assert L.fa_micro_atomic_add(P, 100, 1, None) == 1          # not a multiple of 256
+
+
 def test_status_strings():
     assert fa.status_string(0) == "FA_OK"
     assert fa.status_string(1) == "FA_ERR_INVALID_ARG"
@@ -49,6 +85,7 @@ def fwd(fn="attn_fwd", q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, causal=0
     return getattr(fa.lib(), fn)(q, k, v, o, lse, B, H, N, d, causal, scale, None)
 
 
+@no_gpu_only
 @pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_fp32"])
 def test_forward_rejects_bad_arguments(fn):
     assert fwd(fn, q=0) == fa.FA_ERR_INVALID_ARG
@@ -71,6 +108,7 @@ def bwd(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, ws_bytes=1 << 2
     return fa.lib().attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, N, d, causal, scale, None)
 
 
+@no_gpu_only
 def test_backward_rejects_bad_arguments():
     for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
         assert bwd(**{name: 0}) == fa.FA_ERR_INVALID_ARG, name
@@ -94,6 +132,7 @@ def test_workspace_size():
     assert fa.attn_bwd_workspace_size(1, 1, 16, 96, False) == 0
 
 
+@no_gpu_only
 def test_backward_stages_reject_bad_arguments():
     L = fa.lib()
     need = fa.attn_bwd_workspace_size(1, 1, 16, 64, False)
@@ -114,6 +153,7 @@ def test_backward_stages_reject_bad_arguments():
     assert L.attn_bwd_dq(P, P, P, P, P, need, P, 1, 0, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
 
 
+@no_gpu_only
 def test_gqa_rejects_bad_head_counts():
     L = fa.lib()
     # attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream)
@@ -170,6 +210,7 @@ def test_decode_workspace_size():
     assert L.attn_decode_workspace_size(1, 8, 2, 0, 10, 128) == 0
 
 
+@no_gpu_only
 def test_decode_rejects_bad_arguments():
     assert dec(q=0) == fa.FA_ERR_INVALID_ARG
     assert dec(lse=MIS) == fa.FA_ERR_INVALID_ARG
@@ -191,6 +232,7 @@ def f8(q=P, k=P, vt=P, ldv=128, dq=1.0, dk=1.0, dv=1.0, o=P, lse=P, B=1, H=2, N=
     return fa.lib().attn_fwd_fp8(q, k, vt, ldv, dq, dk, dv, o, lse, B, H, N, d, causal, scale, None)
 
 
+@no_gpu_only
 def test_fp8_rejects_bad_arguments():
     assert f8(q=0) == fa.FA_ERR_INVALID_ARG
     assert f8(vt=MIS) == fa.FA_ERR_INVALID_ARG
