@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     FA_ERR_INVALID_ARG,
     FA_ERR_UNSUPPORTED,
     FA_ERR_WORKSPACE,
+    FA_NOALLOC_SCRATCH_BYTES,
     FA_OK,
     LIB_PATH,
     LIB_POISON_PATH,
@@ -21,6 +22,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_dq,
     attn_bwd_gqa,
     attn_bwd_gqa_workspace_size,
+    attn_bwd_noalloc,
     attn_bwd_prep,
     attn_bwd_workspace_size,
     attn_decode,

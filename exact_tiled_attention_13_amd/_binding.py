@@ -32,7 +32,9 @@ FA_ERR_HIP = 4
 EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_prep",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_size",
             "attn_decode_workspace_size",
-            "attn_decode", "attn_fwd_fp8", "fa_status_string")
+            "attn_decode", "attn_fwd_fp8", "attn_bwd_noalloc", "fa_status_string")
+
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20     # include/fa_mi355x.h
 
 _lock = threading.Lock()
 _lib = None
@@ -104,6 +106,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.attn_decode.restype = ci
     L.attn_fwd_fp8.argtypes = [vp, vp, vp, ci, cf, cf, cf, vp, vp, ci, ci, ci, ci, ci, cf, vp]
     L.attn_fwd_fp8.restype = ci
+    L.attn_bwd_noalloc.argtypes = [vp] * 9 + [ci, ci, ci, ci, ci, cf, vp]
+    L.attn_bwd_noalloc.restype = ci
     L.fa_status_string.argtypes = [ci]
     L.fa_status_string.restype = ctypes.c_char_p
     return L
@@ -206,6 +210,28 @@ def attn_bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
                         _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d,
                         int(bool(causal)), s, _stream(dev))
     _check("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+                     dq=None, dk=None, dv=None):
+    """attn_bwd with the workspace in the library's static device scratch (no workspace argument; the C
+    call allocates nothing). Outputs are allocated here unless given. Returns (dq, dk, dv)."""
+    B, N, H, d = _shape(q)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    s = default_scale(d) if scale is None else float(scale)
+    with torch.cuda.device(dev):
+        st = lib().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, H, N, d, int(bool(causal)), s, _stream(dev))
+    _check("attn_bwd_noalloc", st)
     return dq, dk, dv
 
 

@@ -29,7 +29,8 @@ LIB = os.path.join(PKG, "libfa_mi355x.so")
 LIB_POISON = os.path.join(PKG, "libfa_mi355x_ldspoison.so")
 LIB_MICRO = os.path.join(PKG, "libfa_micro.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_fp32.hip", "fwd_fp8.hip", "bwd_bf16.hip", "decode_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_fp32.hip", "fwd_fp8.hip", "bwd_bf16.hip", "decode_bf16.hip",
+           "noalloc.hip"]
 MICRO_SOURCES = ["micro.hip"]
 
 # (library, sources, extra defines, object-name suffix)

@@ -245,6 +245,32 @@ int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse
                 void* workspace, size_t workspace_bytes,
                 int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, hipStream_t stream);
 
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
+ * memory (code recorded under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same backward, same kernels and
+ * bitwise the same dq, dk, dv, with the workspace taken from a static device
+ * array of FA_NOALLOC_SCRATCH_BYTES inside the library instead of from the
+ * caller. The call allocates and frees nothing.
+ *   Arguments as attn_bwd, without workspace and workspace_bytes; `stream`
+ *   must belong to the current device (hipSetDevice).
+ *   Limit: attn_bwd_workspace_size(B, H, N, d, causal) must not exceed
+ *   FA_NOALLOC_SCRATCH_BYTES (16 MiB: B * H * 64 * ceil(N / 64) up to
+ *   2,097,152 rows, e.g. 16 heads of 131072 tokens); larger shapes return
+ *   FA_ERR_WORKSPACE before any HIP call.
+ *   Sharing: each GPU holds one copy of the array until the process ends,
+ *   and every call on that GPU uses it. Calls that overlap on one GPU (on
+ *   different streams, or from several threads without ordering) race on
+ *   it; order them on one stream or with events. Nothing in it needs
+ *   clearing between calls.
+ *   The first call on a device looks up the array's address there
+ *   (hipGetSymbolAddress); FA_ERR_HIP if that fails.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
 /* fa_status_string -- static, human-readable name of a status code. Never NULL. */
 const char* fa_status_string(int status);
 

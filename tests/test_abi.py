@@ -60,6 +60,21 @@ def test_micro_library_exports_every_declared_symbol():
 
 
 @no_gpu_only
+def test_noalloc_rejects_bad_arguments_before_any_hip_call():
+    L = fa.lib()
+    args = lambda **kw: [kw.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")] + \
+        [kw.get("B", 1), kw.get("H", 2), kw.get("N", 100), kw.get("d", 64), 0, 0.125, None]
+    assert L.attn_bwd_noalloc(*args(q=0)) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_noalloc(*args(dv=MIS)) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_noalloc(*args(d=96)) == fa.FA_ERR_UNSUPPORTED
+    assert L.attn_bwd_noalloc(*args(N=0)) == fa.FA_ERR_INVALID_ARG
+    # 64 heads of 65536 tokens need 32 MiB of statistics: beyond the static scratch.
+    assert fa.attn_bwd_workspace_size(1, 64, 65536, 64) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert L.attn_bwd_noalloc(*args(H=64, N=65536)) == fa.FA_ERR_WORKSPACE
+    assert fa.attn_bwd_workspace_size(1, 16, 131072, 64) <= fa.FA_NOALLOC_SCRATCH_BYTES
+
+
+@no_gpu_only
 def test_micro_rejects_bad_arguments():
     from exact_tiled_attention_13_amd import micro
     L = micro.lib()
