@@ -56,9 +56,10 @@ def counted_fwd(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
-def cpu_baseline(q, k, v, do, scale, heads=2):
+def cpu_baseline(q, k, v, do, scale, heads=2, refs=None):
     """Time the fp64 oracle on a bounded sample of the step: the whole step
-    (forward and backward, both masks) for the first `heads` heads."""
+    (forward and backward, both masks) for the first `heads` heads. The oracle's
+    outputs go into `refs[(causal, h)]` when a dict is given."""
     from threadpoolctl import threadpool_info
 
     from oracle import attn_bwd_head
@@ -70,7 +71,9 @@ def cpu_baseline(q, k, v, do, scale, heads=2):
         qh, kh, vh, gh = (x[0, :, h].double().numpy() for x in (q, k, v, do))
         for causal in (False, True):
             # attn_bwd_head runs the oracle forward (O, LSE) and the backward.
-            attn_bwd_head(qh, kh, vh, gh, causal, scale)
+            r = attn_bwd_head(qh, kh, vh, gh, causal, scale)
+            if refs is not None:
+                refs[(causal, h)] = r
             flops += 3.5 * counted_fwd(1, 1, N, d, causal)
     t1 = time.perf_counter()
     blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
@@ -94,6 +97,33 @@ def cpu_baseline(q, k, v, do, scale, heads=2):
         "blas": ", ".join(f"{i.get('internal_api', '?')} {i.get('version', '')} ({i.get('num_threads', 1)} threads)"
                           for i in blas) or "none found",
     }
+
+
+def step_errors(bufs, refs):
+    """Max normalised error (max |gpu - oracle| / max |oracle| over the checked elements) of the timed
+    step's outputs O, dQ, dK, dV, and the max absolute LSE error, per mask, over the heads in `refs`
+    (whole heads: every query and key row). Runs after the timed region."""
+    import numpy as np
+
+    out = {}
+    for causal in (False, True):
+        hs = sorted(h for (c, h) in refs if c == causal)
+        if not hs:
+            continue
+        b = bufs[causal]
+        got = {n: b[n][0].float().cpu().double().numpy() for n in ("o", "dq", "dk", "dv")}
+        lse = b["lse"][0].cpu().double().numpy()
+        e = {}
+        for n in ("o", "dq", "dk", "dv"):
+            g = np.concatenate([got[n][:, h] for h in hs])
+            r = np.concatenate([refs[(causal, h)][n] for h in hs])
+            e[n] = float(np.abs(g - r).max() / np.abs(r).max())
+        e["lse_abs"] = float(max(np.abs(lse[h] - refs[(causal, h)]["lse"]).max() for h in hs))
+        e["heads"] = hs
+        out["causal" if causal else "noncausal"] = {k: (round(v, 6) if isinstance(v, float) else v)
+                                                    for k, v in e.items()}
+    out["tolerance"] = {"o": 2e-2, "dq_dk_dv": 5e-2, "lse_abs": 1e-3}
+    return out
 
 
 def _raw(name, *args):
@@ -301,12 +331,15 @@ def main():
 
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
           for _ in range(args.steps)]
+    from exact_tiled_attention_13_amd.gpuinfo import ClockSampler, device_facts
+
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler(dev) as clocks:
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(ev[s])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     launch_ms = {n: sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
@@ -384,9 +417,17 @@ def main():
         "passes": passes,
         "kernels": breakdown,
         "roofline": roof,
-        "gpu": torch.cuda.get_device_name(dev),
+        "gpu": device_facts(dev),
+        "clocks_timed_region": clocks.summary(),
         "max_memory_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
     }
+    # The matrix cores' sustained rate on this machine, measured after the timed region (reported beside the
+    # published 2.5 PF denominator, never in its place): back-to-back MFMAs on every SIMD with constant
+    # operands, and with changing pseudo-random operands, whose switching power lowers the clock.
+    from exact_tiled_attention_13_amd import micro
+
+    out["mfma_microbench"] = {f"operands_{name}": micro.mfma_bf16(dev, mode=m)
+                              for name, m in (("constant", 0), ("random", 1))}
     # Report-only: the other 16k-token workloads (head dim 64 at 16k tokens,
     # grouped-query attention at 16k tokens, the short-sequence and mid-length
     # configurations, the batched backward), decoding against a 16k-token
@@ -405,8 +446,16 @@ def main():
 
         report[FP8_LONG.name] = time_fp8(FP8_LONG)
         out["other_workloads"] = report
+    refs = {}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale)
+        out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale, refs=refs)
+    else:
+        # Parity of the timed outputs still checked, on one head per mask.
+        from oracle import attn_bwd_head
+
+        for c in masks:
+            refs[(c, 0)] = attn_bwd_head(*(x[0, :, 0].double().numpy() for x in (q, k, v, do)), c, scale)
+    out["parity_timed_step"] = step_errors(bufs, refs)
     print(json.dumps(out), flush=True)
 
 
