@@ -83,45 +83,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Output rows through LDS. In a 32x32 accumulator whose columns are 32 rows
-// of an output (lane % 32) and whose rows are d (block db), lane (l32, hi)
-// holds elements db*32 + 8g + 4hi .. +3 of row l32 for g = 0..3.
-// stage_rows packs them (times sc) to bf16 and writes them to a 32-row LDS
-// region, 16-byte chunks of a row XOR-swizzled by the row; store_rows reads
-// back whole 16-byte chunks and writes rows r0 .. r0+31 (those below n) of
-// g (row stride rs elements), so that each store instruction covers
-// contiguous rows instead of 8 bytes of 32 rows. The region belongs to one
-// wave; LDS operations of a wave run in order, so no barrier is needed
-// between the two.
-template <int D>
-__device__ __forceinline__ void stage_rows(unsigned char* sw, const f32x16 (&acc)[D / 32], float sc, int l32,
-                                           int hi) {
-    constexpr int RB = D * 2, CPR = RB / 16;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            u32x2 w;
-            w[0] = pack_bf16x2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc);
-            w[1] = pack_bf16x2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
-            *reinterpret_cast<u32x2*>(sw + l32 * RB + (((db * 4 + g) ^ (l32 & (CPR - 1))) << 4) + 8 * hi) = w;
-        }
-}
-
-template <int D>
-__device__ __forceinline__ void store_rows(__bf16* g, size_t rs, const unsigned char* sw, int r0, int n,
-                                           int lane) {
-    constexpr int RB = D * 2, CPR = RB / 16;
-#pragma unroll
-    for (int j = 0; j < 32 * CPR / 64; ++j) {
-        const int i = j * 64 + lane;
-        const int row = i / CPR, ch = i % CPR;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sw + row * RB + ((ch ^ (row & (CPR - 1))) << 4));
-        if (r0 + row < n) st16(g + (size_t)(r0 + row) * rs + ch * 8, v);
-    }
-}
-
-// ---------------------------------------------------------------------------
 // dK, dV for d = 64: one workgroup of 4 waves per 128 keys (32 per wave, K
 // and V rows in VGPRs; two workgroups share a CU), looping over query tiles
 // of 64 rows staged in LDS by direct loads.
@@ -215,11 +176,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     unsigned toff[T::NINST / NW];
     T::template offsets<NW>(toff, rs, wave, lane);
     // Stage s receives query tile t of group head g.
+    const uint32_t qspan = T::span(rs, N);
     auto dma = [&](int g, int t, int s) {
         unsigned char* st = stage_ptr(s);
         const int q0 = qstart + t * BQ;
-        T::template load<NW>(st, Qg0 + (size_t)g * D, rs, q0, N, wave, lane, toff);
-        T::template load<NW>(st + T::BYTES, dOg0 + (size_t)g * D, rs, q0, N, wave, lane, toff);
+        if (GQA && g > 0) {
+            T::template load<NW>(st, Qg0 + (size_t)g * D, rs, q0, N, wave, lane, toff);
+            T::template load<NW>(st + T::BYTES, dOg0 + (size_t)g * D, rs, q0, N, wave, lane, toff);
+        } else {
+            T::template load_buf<NW>(st, Qg0, qspan, rs, q0, N, wave, lane, toff);
+            T::template load_buf<NW>(st + T::BYTES, dOg0, qspan, rs, q0, N, wave, lane, toff);
+        }
         // q0 + 63 < npad: the padded statistics need no clamp.
         const size_t so = stat0 + (size_t)g * npad + q0 + lane;
         if (wave == 0)
@@ -560,11 +527,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     unsigned toff[T::NINST / NL];
     T::template offsets<NL>(toff, rs, kg, lane);
     // Tile t of group head g: Q into Q stage qs, dO and statistics into stage gs.
+    // Query head 0 of the group part loads through a buffer resource over its rows.
+    const uint32_t qspan = T::span(rs, N);
     auto dma = [&](int g, int t, int qs, int gs) {
         if (!pwave) return;
         const int q0 = qstart + t * BQ;
-        T::template load<NL>(qtile(qs), Qg0 + (size_t)g * D, rs, q0, N, kg, lane, toff);
-        T::template load<NL>(gtile(gs), dOg0 + (size_t)g * D, rs, q0, N, kg, lane, toff);
+        if (GQA && g > 0) {
+            T::template load<NL>(qtile(qs), Qg0 + (size_t)g * D, rs, q0, N, kg, lane, toff);
+            T::template load<NL>(gtile(gs), dOg0 + (size_t)g * D, rs, q0, N, kg, lane, toff);
+        } else {
+            T::template load_buf<NL>(qtile(qs), Qg0, qspan, rs, q0, N, kg, lane, toff);
+            T::template load_buf<NL>(gtile(gs), dOg0, qspan, rs, q0, N, kg, lane, toff);
+        }
         // q0 + 63 < npad: the padded statistics need no clamp.
         const size_t so = stat0 + (size_t)g * npad + q0 + lane;
         if (kg == 0) __builtin_amdgcn_global_load_lds(a.lse2 + so, (lds_void_t*)stats(gs), 4, 0, 0);
@@ -835,7 +809,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 // tiles; dQ^T += K^T dS^T takes its A operand from transposing reads of the
 // same K tile. The accumulators hold one query per lane, as in the forward.
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     using T = LdsTile<D>;
     constexpr int BM = NW * 32;          // queries per workgroup
     constexpr int BN = T::ROWS;          // keys per tile
@@ -906,9 +880,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     auto vbuf = [&](int s) { return smem + (2 + s) * T::BYTES; };
     unsigned toff[T::NINST / NW];
     T::template offsets<NW>(toff, rskv, wave, lane);
+    const uint32_t kvspan = T::span(rskv, N);
     auto dma = [&](int t, int s) {
-        T::template load<NW>(kbuf(s), Kg, rskv, t * BN, N, wave, lane, toff);
-        T::template load<NW>(vbuf(s), Vg, rskv, t * BN, N, wave, lane, toff);
+        T::template load_buf<NW>(kbuf(s), Kg, kvspan, rskv, t * BN, N, wave, lane, toff);
+        T::template load_buf<NW>(vbuf(s), Vg, kvspan, rskv, t * BN, N, wave, lane, toff);
     };
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
@@ -1071,9 +1046,9 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
-    // 4-wave workgroups (two per CU) for d = 64 and for d = 128 up to 2048
-    // tokens, as in the forward (measured: 5-26% faster there; 8 waves win
-    // for d = 128 from 4096 tokens on).
+    // 4-wave workgroups (two per CU at d = 128, three at d = 64) for d = 64
+    // and for d = 128 up to 2048 tokens, as in the forward (measured: 5-26%
+    // faster there; 8 waves win for d = 128 from 4096 tokens on).
     if constexpr (D == 128) {
         if (a.N > 2048) {
             const long long g = (long long)((a.N + 255) / 256) * a.B * a.H;

@@ -150,6 +150,15 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3:
+// 32-bit elements, no swizzle, no stride). Loads through it take a per-lane
+// 32-bit offset and a uniform offset held in an SGPR, so a tile load whose
+// per-lane offsets repeat from tile to tile needs no per-lane address
+// arithmetic (a 64-bit address per lane costs a VALU add per load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Materialises x in a VGPR at this point of the program: the computation of x
 // can no longer be sunk past it (the value itself is unchanged). Used to keep
 // running sums spread over a hand-scheduled loop instead of being gathered

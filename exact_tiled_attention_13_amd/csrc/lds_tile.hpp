@@ -19,6 +19,15 @@ namespace fa {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
+// One 16-byte-per-lane direct-to-LDS load through a buffer resource over
+// `bytes` bytes at `base`: lane i's 16 bytes at byte offset voff + soff land
+// in LDS slot i of the 1 KB at dst.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t bytes, unsigned char* dst, uint32_t voff,
+                                                  uint32_t soff) {
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(base, bytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, voff, soff, 0, 0);
+}
+
 template <int D, int ROWS_ = 64>
 struct LdsTile {
     static_assert(ROWS_ % 16 == 0, "tiles are whole 16-row swizzle groups");
@@ -74,6 +83,30 @@ struct LdsTile {
         }
     }
 
+    // The same through a buffer resource over `bytes` bytes of g's rows (row
+    // stride rs): whole tiles add the uniform row0 * rs in an SGPR to each
+    // lane's fixed offset, with no per-lane address arithmetic; the ragged
+    // last tile takes load()'s clamped path. A head's rows span less than
+    // 2^32 bytes, so the 32-bit offsets hold. (The resource is rebuilt from
+    // uniform values at each call; the compiler keeps it in SGPRs.)
+    template <int NW>
+    __device__ static __forceinline__ void load_buf(unsigned char* dst, const __bf16* g, uint32_t bytes, size_t rs,
+                                                    int row0, int n, int w, int lane,
+                                                    const unsigned (&off)[NINST / NW]) {
+        if (row0 + ROWS <= n) {
+            const uint32_t so = (uint32_t)row0 * (uint32_t)rs * 2u;
+#pragma unroll
+            for (int j = 0; j < NINST / NW; ++j) buffer_load_lds16(g, bytes, dst + (w + NW * j) * 1024, off[j] * 2u, so);
+        } else {
+            load<NW>(dst, g, rs, row0, n, w, lane, off);
+        }
+    }
+
+    // Bytes of a head's rows 0 .. n-1 (row stride rs elements) from its first element.
+    __device__ static __forceinline__ uint32_t span(size_t rs, int n) {
+        return (uint32_t)(((size_t)(n - 1) * rs + D) * 2);
+    }
+
     // Row reads: A/B operand of a 32x32x16 MFMA whose 32 rows are tile rows
     // rb*32 + lane%32 and whose K step cc covers d = cc*16 + (lane/32)*8 .. +8.
     // Byte offset = rowbase(lane) ^ (cc << 5), plus rb*32*RB.
@@ -106,5 +139,44 @@ struct LdsTile {
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 };
+
+// ---------------------------------------------------------------------------
+// Output rows through LDS. In a 32x32 accumulator whose columns are 32 rows
+// of an output (lane % 32) and whose rows are d (block db), lane (l32, hi)
+// holds elements db*32 + 8g + 4hi .. +3 of row l32 for g = 0..3.
+// stage_rows packs them (times sc) to bf16 and writes them to a 32-row LDS
+// region, 16-byte chunks of a row XOR-swizzled by the row; store_rows reads
+// back whole 16-byte chunks and writes rows r0 .. r0+31 (those below n) of
+// g (row stride rs elements), so that each store instruction covers
+// contiguous rows instead of 8 bytes of 32 rows. The region belongs to one
+// wave; LDS operations of a wave run in order, so no barrier is needed
+// between the two.
+template <int D>
+__device__ __forceinline__ void stage_rows(unsigned char* sw, const f32x16 (&acc)[D / 32], float sc, int l32,
+                                           int hi) {
+    constexpr int RB = D * 2, CPR = RB / 16;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc);
+            w[1] = pack_bf16x2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
+            *reinterpret_cast<u32x2*>(sw + l32 * RB + (((db * 4 + g) ^ (l32 & (CPR - 1))) << 4) + 8 * hi) = w;
+        }
+}
+
+template <int D>
+__device__ __forceinline__ void store_rows(__bf16* g, size_t rs, const unsigned char* sw, int r0, int n,
+                                           int lane) {
+    constexpr int RB = D * 2, CPR = RB / 16;
+#pragma unroll
+    for (int j = 0; j < 32 * CPR / 64; ++j) {
+        const int i = j * 64 + lane;
+        const int row = i / CPR, ch = i % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sw + row * RB + ((ch ^ (row & (CPR - 1))) << 4));
+        if (r0 + row < n) st16(g + (size_t)(r0 + row) * rs + ch * 8, v);
+    }
+}
 
 }  // namespace fa
