@@ -90,6 +90,52 @@ __global__ __launch_bounds__(256) void micro_mfma_bf16_kernel(float* out, unsign
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// MFMAs interleaved with a wave's own VALU work: each MFMA (four chains, random
+// register operands as in mode 1) is followed by NF independent v_fma_f32 and
+// NE v_exp_f32 on eight other registers, fenced so the compiler keeps the
+// order. Run with two workgroups of four waves per CU (two waves per SIMD),
+// the attention kernels' occupancy; compare with the plain MFMA stream.
+template <int NF, int NE>
+__global__ __launch_bounds__(256, 2) void micro_mfma_valu_kernel(float* out, unsigned long long* clk, int iters) {
+    const uint32_t seed = (blockIdx.x * 256u + threadIdx.x) * 64u;
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[r][i] = rnd_bf16(seed + 16 * r + i);
+            b[r][i] = rnd_bf16(seed + 16 * r + 8 + i);
+        }
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.001f * (float)(threadIdx.x + j);
+    const float cf = 0.999f, cb = 0.0001f;
+    f32x16 c[4] = {};
+    unsigned long long t0, r0;
+    stamp_begin(t0, r0);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            c[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b[r], c[r], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < NF; ++k) v[k % 8] = __builtin_fmaf(v[k % 8], cf, cb);
+#pragma unroll
+            for (int k = 0; k < NE; ++k) v[(k + 4) % 8] = __builtin_amdgcn_exp2f(-v[(k + 4) % 8]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    stamp_end(clk, t0, r0);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += c[r][i];
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 __global__ __launch_bounds__(256) void micro_exp2_kernel(float* out, unsigned long long* clk, int iters) {
     float x[8];
 #pragma unroll
@@ -154,6 +200,20 @@ int fa_micro_mfma_bf16(float* out, unsigned long long* clk, int blocks, int iter
     else
         return kInvalid;
     return hipGetLastError() == hipSuccess ? kOk : kHip;
+}
+
+int fa_micro_mfma_valu(float* out, unsigned long long* clk, int blocks, int iters, int nfma, int nexp,
+                       hipStream_t stream) {
+    if (!aligned16(out) || !aligned16(clk) || blocks < 1 || iters < 1 || iters > (1 << 24)) return kInvalid;
+#define FA_MV(F, E)                                                                                          \
+    if (nfma == F && nexp == E) {                                                                           \
+        hipLaunchKernelGGL((micro_mfma_valu_kernel<F, E>), dim3((unsigned)blocks), dim3(256), 0, stream, out, clk, \
+                           iters);                                                                          \
+        return hipGetLastError() == hipSuccess ? kOk : kHip;                                               \
+    }
+    FA_MV(0, 0) FA_MV(2, 0) FA_MV(4, 0) FA_MV(8, 0) FA_MV(0, 1) FA_MV(0, 2) FA_MV(0, 4) FA_MV(4, 2) FA_MV(6, 2)
+#undef FA_MV
+    return kInvalid;
 }
 
 int fa_micro_exp2(float* out, unsigned long long* clk, int blocks, int iters, hipStream_t stream) {

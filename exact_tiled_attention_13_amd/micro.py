@@ -38,6 +38,8 @@ def lib() -> ctypes.CDLL:
             vp, ci, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
             L.fa_micro_mfma_bf16.argtypes = [vp, vp, ci, ci, ci, vp]
             L.fa_micro_exp2.argtypes = [vp, vp, ci, ci, vp]
+            L.fa_micro_mfma_valu.argtypes = [vp, vp, ci, ci, ci, ci, vp]
+            L.fa_micro_mfma_valu.restype = ci
             L.fa_micro_fp8_dot.argtypes = [vp, vp, vp, ci, ci, vp]
             L.fa_micro_atomic_add.argtypes = [vp, ll, ci, vp]
             for f in (L.fa_micro_mfma_bf16, L.fa_micro_exp2, L.fa_micro_fp8_dot, L.fa_micro_atomic_add):
@@ -98,6 +100,24 @@ def mfma_bf16(dev=None, blocks_per_cu: int = 4, iters: int = 40000, reps: int = 
             "cus": cus, "blocks": blocks, "iters": iters}
 
 
+def mfma_with_valu(dev=None, nfma: int = 0, nexp: int = 0, iters: int = 20000, reps: int = 3) -> dict:
+    """MFMA rate when each MFMA of a wave is followed by `nfma` v_fma_f32 and `nexp` v_exp_f32 of its own
+    (two waves per SIMD, random operands): how much VALU work a wave can place between its MFMAs for free."""
+    dev = dev or torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = cus * 2
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clk = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+    ms = _timed(dev, lambda: lib().fa_micro_mfma_valu(out.data_ptr(), clk.data_ptr(), blocks, iters, nfma, nexp,
+                                                      _stream(dev)), reps)
+    flop = blocks * 4.0 * iters * 4 * FLOP_PER_MFMA_32x32x16
+    ghz = clock_ghz(clk)
+    tflops = flop / ms / 1e9
+    at_clock = cus * 4 * 1024 * ghz * 1e9 / 1e12
+    return {"nfma": nfma, "nexp": nexp, "tflops": round(tflops, 1), "clock_ghz": round(ghz, 3),
+            "util_at_clock": round(tflops / at_clock, 4), "ms": round(ms, 3)}
+
+
 def exp2_rate(dev=None, blocks_per_cu: int = 4, iters: int = 20000, reps: int = 3) -> dict:
     """Issue rate of v_exp_f32 (eight independent chains per lane): clocks per wave instruction per SIMD."""
     dev = dev or torch.device("cuda:0")
@@ -139,6 +159,8 @@ def main():
     dev = torch.device("cuda:0")
     res = {f"mfma_bf16_mode{m}": mfma_bf16(dev, mode=m) for m in (0, 1, 2)}
     res.update({"exp2": exp2_rate(dev), "atomic_add_f32": atomic_add(dev)})
+    res["mfma_with_valu"] = [mfma_with_valu(dev, f, e) for f, e in ((0, 0), (2, 0), (4, 0), (8, 0), (0, 1), (0, 2),
+                                                                    (0, 4), (4, 2), (6, 2))]
     print(json.dumps(res), flush=True)
 
 

@@ -54,6 +54,18 @@ extern "C" {
 int fa_micro_mfma_bf16(float* out, unsigned long long* clk, int blocks, int iters, int mode, hipStream_t stream);
 
 /*
+ * fa_micro_mfma_valu -- whether a wave's own VALU work hides under its MFMAs:
+ * `blocks` workgroups of 256 threads (launched for two waves per SIMD); each
+ * wave runs `iters` rounds of four v_mfma_f32_32x32x16_bf16 (random register
+ * operands, four chains), each followed by `nfma` independent v_fma_f32 and
+ * `nexp` v_exp_f32. (nfma, nexp) in {(0,0), (2,0), (4,0), (8,0), (0,1),
+ * (0,2), (0,4), (4,2), (6,2)}. out: blocks * 256 floats; clk: 4 * blocks
+ * words. FLOP = blocks * 4 * iters * 4 * 32768.
+ */
+int fa_micro_mfma_valu(float* out, unsigned long long* clk, int blocks, int iters, int nfma, int nexp,
+                       hipStream_t stream);
+
+/*
  * fa_micro_exp2 -- `blocks` workgroups of 256 threads; each lane runs eight
  * independent chains x <- exp2(-x) for `iters` steps (one v_exp_f32 each).
  * out: blocks * 256 floats. clk: 4 * blocks words. Instructions per wave:

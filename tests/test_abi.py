@@ -53,7 +53,8 @@ def test_micro_library_exports_every_declared_symbol():
     from exact_tiled_attention_13_amd import micro
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fa_micro.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", text, flags=re.M)))
-    assert names == ["fa_micro_atomic_add", "fa_micro_exp2", "fa_micro_fp8_dot", "fa_micro_mfma_bf16"]
+    assert names == ["fa_micro_atomic_add", "fa_micro_exp2", "fa_micro_fp8_dot", "fa_micro_mfma_bf16",
+                     "fa_micro_mfma_valu"]
     L = ctypes.CDLL(micro.LIB_MICRO)
     for name in names:
         assert hasattr(L, name), name
@@ -82,6 +83,7 @@ def test_micro_rejects_bad_arguments():
     assert L.fa_micro_mfma_bf16(P, P, 4, 3, 0, None) == 1       # odd iteration count
     assert L.fa_micro_mfma_bf16(P, P, 4, 2, 3, None) == 1       # unknown operand mode
     assert L.fa_micro_exp2(P, P, 0, 1, None) == 1
+    assert L.fa_micro_mfma_valu(P, P, 4, 10, 3, 0, None) == 1   # unsupported mix
     assert L.fa_micro_fp8_dot(P, P, P, 1, 65, None) == 1
     assert L.fa_micro_fp8_dot(P, MIS, P, 1, 1, None) == 1
     assert L.fa_micro_atomic_add(P, 100, 1, None) == 1          # not a multiple of 256
