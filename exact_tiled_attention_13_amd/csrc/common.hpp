@@ -168,6 +168,16 @@ __device__ __forceinline__ void pin_vgpr(float& x) {
     asm volatile("" : "+v"(x));
 #endif
 }
+__device__ __forceinline__ void pin_vgpr(int& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(x));
+#endif
+}
+__device__ __forceinline__ void pin_vgpr(uint32_t& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(x));
+#endif
+}
 
 // Round-to-nearest-even fp32 pair -> packed bf16 pair (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

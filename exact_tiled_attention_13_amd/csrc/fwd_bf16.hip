@@ -27,9 +27,9 @@
 //                 lane, so the online-softmax rescale is a per-lane scalar.
 //   Softmax in base 2: p = exp2(S * c2 - m) with c2 = |scale| * log2(e); a
 //   negative scale is folded into the sign bits of Q.
-//   K/V tiles are double-buffered in LDS and fetched by direct-to-LDS loads
-//   (global_load_lds, 16 bytes per lane) one step ahead of their use; one
-//   barrier per tile.
+//   K/V tiles are fetched into LDS by direct-to-LDS loads (16 bytes per
+//   lane) one step ahead of their use, double-buffered (V in four buffers in
+//   the 8-wave ping-pong form); one barrier per tile.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -65,15 +65,28 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     constexpr int RB = D * 2;             // bytes per K/V row
     constexpr int TILE = BN * RB;         // bytes per K or V tile
     constexpr int NINST = TILE / 1024;    // 1 KB direct-to-LDS wave loads per tile
-    constexpr int IPW = NINST / NW;       // ... per wave
+    // Ping-pong (8 waves at d = 128, the workgroup alone on its CU): waves
+    // 4-7 run half a step behind waves 0-3 (see the main loop), so that on
+    // each SIMD, which holds one wave of each half, one wave's exponentials
+    // overlap the other's P V products instead of both waves reaching the
+    // same phase together after every barrier. Waves 0-3 issue all the tile
+    // loads.
+    constexpr bool PP = D == 128 && NW == 8;
+    constexpr int NL = PP ? NW / 2 : NW;  // waves that issue the tile loads
+    constexpr int IPW = NINST / NL;       // ... per loading wave
     constexpr int RPI = 1024 / RB;        // rows covered by one such load
     constexpr int CPR = RB / 16;          // 16-byte chunks per row
     constexpr int DC = D / 16;            // 16-wide d chunks (MFMA K steps of S)
     constexpr int KB = BN / 32;           // 32-key blocks per tile
     constexpr int DB = D / 32;            // 32-wide d blocks of O^T
-    static_assert(IPW * NW == NINST && IPW >= 1, "tile must split evenly over the waves");
+    static_assert(IPW * NL == NINST && IPW >= 1, "tile must split evenly over the waves");
+    // V buffers: tile j in slot j % NVB. The ping-pong form needs three at a
+    // time (V_{t-1}, V_t read while V_{t+1} arrives); four keep the slot a
+    // compile-time constant in a loop body unrolled over U = 4 steps.
+    constexpr int NVB = PP ? 4 : 2;
+    constexpr int U = PP ? 4 : 2;
 
-    // LDS: Kbuf[0], Kbuf[1], Vbuf[0], Vbuf[1]; rows unpadded, 16-byte chunks
+    // LDS: Kbuf[0], Kbuf[1], Vbuf[0 .. NVB-1]; rows unpadded, 16-byte chunks
     // XOR-swizzled per row (see swk / swv) so that the MFMA operand reads are
     // free of bank conflicts.
     // Q enters through LDS as well (see below) where the extra LDS still
@@ -81,7 +94,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     // waves, whose two workgroups per CU already take 128 KB.
     constexpr bool QLDS = D == 64;
     constexpr int QST = QLDS ? NW * 32 * RB : 0;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE + QST];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[(2 + NVB) * TILE + QST];
     lds_poison(smem, sizeof(smem));
 
     const int B = a.B, H = a.H, N = a.N;
@@ -120,7 +133,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     // read from there after the prologue's barrier; otherwise each lane
     // loads its own row.
     bf16x8 qf[DC];
-    unsigned char* qst = smem + 4 * TILE + wave * 32 * RB;
+    unsigned char* qst = smem + (2 + NVB) * TILE + wave * 32 * RB;
     auto qdma = [&] {
 #pragma unroll
         for (int j = 0; j < 32 * CPR / 64; ++j) {
@@ -164,7 +177,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     // covers the rows of load j shifted by NW * RPI (a multiple of that
     // group), so one per-lane offset per tensor serves every load of the
     // tile; load j adds the uniform j * NW * RPI rows.
-    static_assert((NW * RPI) % 16 == 0, "wave loads must keep the row swizzle");
+    static_assert((NL * RPI) % 16 == 0, "wave loads must keep the row swizzle");
     unsigned koff0, voff0;
     {
         const int row = wave * RPI + lane / CPR;
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kg, span), vrs = buffer_rsrc(Vg, span);
     const uint32_t koffb = koff0 * 2u, voffb = voff0 * 2u;
     const uint32_t tile_b = (uint32_t)BN * (uint32_t)rskv * 2u;          // bytes per tile of rows
-    const uint32_t jstep_b = (uint32_t)(NW * RPI) * (uint32_t)rskv * 2u;  // bytes between load j and j + 1
+    const uint32_t jstep_b = (uint32_t)(NL * RPI) * (uint32_t)rskv * 2u;  // bytes between load j and j + 1
     // (The 4-wave d = 128 form keeps 64-bit per-lane addresses: measured 2-4%
     // faster there with them.)
     constexpr bool BUFLOAD = !(D == 128 && NW == 4);
@@ -189,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
             const uint32_t so = (uint32_t)t * tile_b;
 #pragma unroll
             for (int j = 0; j < IPW; ++j) {
-                const int inst = wave + NW * j;
+                const int inst = wave + NL * j;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? vrs : krs,
                                                          (lds_void_t*)(smem + buf * TILE + inst * 1024), 16,
                                                          is_v ? voffb : koffb, so + j * jstep_b, 0, 0);
@@ -198,14 +211,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
             const __bf16* gt = g + (size_t)t * BN * rskv;
 #pragma unroll
             for (int j = 0; j < IPW; ++j) {
-                const int inst = wave + NW * j;
-                __builtin_amdgcn_global_load_lds(gt + j * (size_t)(NW * RPI) * rskv + (size_t)(is_v ? voff0 : koff0),
+                const int inst = wave + NL * j;
+                __builtin_amdgcn_global_load_lds(gt + j * (size_t)(NL * RPI) * rskv + (size_t)(is_v ? voff0 : koff0),
                                                  (lds_void_t*)(smem + buf * TILE + inst * 1024), 16, 0, 0);
             }
         } else {
 #pragma unroll
             for (int j = 0; j < IPW; ++j) {
-                const int inst = wave + NW * j;
+                const int inst = wave + NL * j;
                 const int row = inst * RPI + lane / CPR;
                 const int slot = lane % CPR;
                 const int c = slot ^ (is_v ? swv(row) : swk(row));
@@ -217,6 +230,12 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     };
     auto kbuf = [&](int i) { return smem + i * TILE; };
     auto vbuf = [&](int i) { return smem + (2 + i) * TILE; };
+    // The loads of step t, issued as it starts: K_{t+2} and V_{t+1}.
+    auto issue = [&](int t) {
+        if (t + 2 < ntiles) dma(Kg, t + 2, t & 1, false);
+        if (t + 1 < ntiles) dma(Vg, t + 1, 2 + (t + 1) % NVB, true);
+    };
+    const bool lag = PP && wave >= 4;     // a lagging wave (ping-pong)
 
     // Per-lane byte offsets of the MFMA operand reads. The swizzle only flips
     // address bits that the row base leaves clear, so the offset of d chunk cc
@@ -236,6 +255,12 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     }
 
     auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+    int vhi[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        vhi[db] = (vbase ^ (db << 6)) + 2 * TILE;
+        if constexpr (PP) pin_vgpr(vhi[db]);
+    }
 
     auto scores = [&](f32x16 (&s)[KB], const unsigned char* Ks) {
 #pragma unroll
@@ -295,7 +320,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     // tile t+1 are interleaved with the exponentials of tile t (phase A, run
     // at raised wave priority so that the VALU-heavy phase of one wave is
     // not starved by the other wave's PV MFMAs), then the PV MFMAs of tile t
-    // run (phase B). K operands are read in batches of KBS MFMAs one batch
+    // run (phase B). Between two barriers a leading wave runs A(t) then B(t)
+    // and, in the ping-pong form, a lagging one B(t-1) then A(t): its barrier
+    // falls between its A and B. In that interval the leading waves read V_t,
+    // the lagging ones V_{t-1}, and V_{t+1} arrives; the leading waves issue
+    // the interval's loads and wait for them before its closing barrier. K operands are read in batches of KBS MFMAs one batch
     // ahead (while a direct-to-LDS load is in flight the compiler can only
     // wait for all outstanding LDS reads, so reads issued one MFMA ahead
     // would be waited for at once); V operands PFV MFMAs ahead. For the last
@@ -306,13 +335,15 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     constexpr int KBS = 2;
     constexpr int PFV = 2;
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    auto step = [&](int t, f32x16 (&scur)[KB], f32x16 (&snext)[KB], auto masked_c) {
-        if (t + 2 < ntiles) dma(Kg, t + 2, t & 1, false);
-        if (t + 1 < ntiles) dma(Vg, t + 1, 2 + ((t + 1) & 1), true);
+    // In the ping-pong form R = t % U is known at compile time; otherwise the
+    // buffer slots follow t at run time.
+    auto step = [&](int t, f32x16 (&scur)[KB], f32x16 (&snext)[KB], auto masked_c, auto r_c) {
+        constexpr int R = decltype(r_c)::value;
+        if (!lag) issue(t);
         // Phase A. Score MFMA i: block i % KB, d chunk i / KB (two chains).
         // K operands are read in batches of KBS MFMAs, one batch ahead; the
         // first batch is in flight during prepare.
-        const unsigned char* Ks = kbuf((t + 1) & 1);
+        const unsigned char* Ks = kbuf(PP ? (R + 1) & 1 : (t + 1) & 1);
         auto kread = [&](int i) {
             return *reinterpret_cast<const bf16x8*>(Ks + (i % KB) * 32 * RB + (kbase ^ ((i / KB) << 5)));
         };
@@ -361,7 +392,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
                 const int f = 2 * q;
                 rsum[q % 2] += e[q][0] + e[q][1];
                 pin_vgpr(rsum[q % 2]);
-                w[f / 8][(f % 8) / 2] = pack_bf16x2(e[q][0], e[q][1]);
+                uint32_t pw = pack_bf16x2(e[q][0], e[q][1]);
+                // Keeps the pack in phase A (not sunk past a lagging wave's
+                // barrier into phase B).
+                if constexpr (PP) pin_vgpr(pw);
+                w[f / 8][(f % 8) / 2] = pw;
                 if (f % 8 == 6) pb[f / 8] = as_bf16x8(w[f / 8]);
             }
         };
@@ -382,12 +417,22 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
             fence();
         }
         l += rsum[0] + rsum[1];
+        if (lag) {
+            // A lagging wave's barrier: phase A of tile t is done, phase B
+            // follows in the next interval.
+            __builtin_amdgcn_s_setprio(0);
+            __syncthreads();
+        }
 
         // Phase B. PV MFMA j: key chunk j / DB, d block j % DB.
-        const unsigned char* Vs = vbuf(t & 1);
+        // Above 64 KB of LDS (the upper V buffers of the ping-pong form) a
+        // buffer's offset no longer fits a read's immediate offset: there the
+        // reads start from the pinned per-d-block bases vhi (V region
+        // included) and only the slot and chunk offsets stay immediate.
+        const unsigned char* Vs = PP ? smem + (R % NVB) * TILE : vbuf(t & 1);
         auto vread = [&](int j) {
             const int kc = j / DB, db = j % DB;
-            const int voff = (vbase ^ (db << 6)) + kc * 16 * RB;
+            const int voff = (PP ? vhi[db] : (vbase ^ (db << 6))) + kc * 16 * RB;
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vs + voff));
             const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vs + voff + 8 * RB));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -403,14 +448,18 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
             if (j + PFV < NP) vfr[j + PFV] = vread(j + PFV);
             fence();
         }
-        wait_dma();
-        __syncthreads();
+        if (!lag) {
+            wait_dma();
+            __syncthreads();
+        }
     };
 
     // Prologue: K_0, V_0, K_1 into LDS, then S_0.
-    dma(Kg, 0, 0, false);
-    dma(Vg, 0, 2, true);
-    if (ntiles > 1) dma(Kg, 1, 1, false);
+    if (!lag) {
+        dma(Kg, 0, 0, false);
+        dma(Vg, 0, 2, true);
+        if (ntiles > 1) dma(Kg, 1, 1, false);
+    }
     wait_dma();
     __syncthreads();
     if constexpr (QLDS) {
@@ -424,43 +473,100 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     }
     f32x16 sa[KB], sb[KB];
     scores(sa, kbuf(0));
-    __syncthreads();   // Kbuf[0] receives K_2 in iteration 0
+    __syncthreads();   // Kbuf[0] receives K_2 in step 0
 
     // Tiles before t_split need no mask for any wave (they end before the
     // workgroup's first query and before N); the rest run the masked variant.
     // Causal waves whose rows all precede a tile run it fully masked (p = 0).
     const int t_split = min(CAUSAL ? q0 / BN : ntiles, (N % BN) ? ntiles - 1 : ntiles);
-    int t = 0;
-    for (; t + 1 < t_split; t += 2) {
-        step(t, sa, sb, std::false_type{});
-        step(t + 1, sb, sa, std::false_type{});
-    }
-    if (t < t_split) {
-        step(t, sa, sb, std::false_type{});
-        ++t;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
-    }
+    // Step t runs with S_t in sa when t is even, in sb when odd.
+    auto run = [&](int t, auto r_c, auto masked_c) {
+        if constexpr (decltype(r_c)::value & 1)
+            step(t, sb, sa, masked_c, r_c);
+        else
+            step(t, sa, sb, masked_c, r_c);
+    };
+    using R0 = std::integral_constant<int, 0>;
+    using R1 = std::integral_constant<int, 1>;
+    using R2 = std::integral_constant<int, 2>;
+    using R3 = std::integral_constant<int, 3>;
     // Under the causal mask a wave stops computing at the first tile whose
     // keys all follow its last query (that tile and every later one give
     // p = 0), but keeps issuing its share of the loads and passing the
     // barriers until the workgroup is done.
     auto idle = [&](int tt) { return CAUSAL && tt * BN > qw + 31; };
-    for (; t < ntiles; t += 2) {
-        if (idle(t)) break;
-        step(t, sa, sb, std::true_type{});
-        if (t + 1 < ntiles) {
-            if (idle(t + 1)) {
-                ++t;
+    if constexpr (!PP) {
+        int t = 0;
+        for (; t + 1 < t_split; t += 2) {
+            step(t, sa, sb, std::false_type{}, R0{});
+            step(t + 1, sb, sa, std::false_type{}, R0{});
+        }
+        if (t < t_split) {
+            step(t, sa, sb, std::false_type{}, R0{});
+            ++t;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
+        }
+        for (; t < ntiles; t += 2) {
+            if (idle(t)) break;
+            step(t, sa, sb, std::true_type{}, R0{});
+            if (t + 1 < ntiles) {
+                if (idle(t + 1)) {
+                    ++t;
+                    break;
+                }
+                step(t + 1, sb, sa, std::true_type{}, R0{});
+            }
+        }
+        for (; t < ntiles; ++t) {
+            issue(t);
+            wait_dma();
+            __syncthreads();
+        }
+    } else {
+        // The unmasked steps run in whole unrolled bodies; the up to U - 1 that
+        // remain join the masked ones (on a tile with nothing to mask the mask
+        // changes no score).
+        const int t_un = t_split - t_split % U;
+        int t = 0;
+        for (; t < t_un; t += U) {
+            run(t, R0{}, std::false_type{});
+            run(t + 1, R1{}, std::false_type{});
+            if constexpr (U == 4) {
+                run(t + 2, R2{}, std::false_type{});
+                run(t + 3, R3{}, std::false_type{});
+            }
+        }
+        // Masked steps, from a multiple of U; on leaving, t is the first step
+        // not run.
+        auto masked = [&](int tt, auto r_c) {
+            if (tt >= ntiles || idle(tt)) return false;
+            run(tt, r_c, std::true_type{});
+            return true;
+        };
+        for (; t < ntiles; t += U) {
+            if (!masked(t, R0{})) break;
+            if (!masked(t + 1, R1{})) {
+                t += 1;
                 break;
             }
-            step(t + 1, sb, sa, std::true_type{});
+            if constexpr (U == 4) {
+                if (!masked(t + 2, R2{})) {
+                    t += 2;
+                    break;
+                }
+                if (!masked(t + 3, R3{})) {
+                    t += 3;
+                    break;
+                }
+            }
         }
-    }
-    for (; t < ntiles; ++t) {
-        if (t + 2 < ntiles) dma(Kg, t + 2, t & 1, false);
-        if (t + 1 < ntiles) dma(Vg, t + 1, 2 + ((t + 1) & 1), true);
-        wait_dma();
+        for (; t < ntiles; ++t) {
+            if (!lag) issue(t);
+            wait_dma();
+            __syncthreads();
+        }
+        // The lagging waves run B of their last tile after the last barrier.
         __syncthreads();
     }
 
@@ -472,7 +578,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     // rows per instruction.
     const float lt = sum_halves(l);
     const float inv = 1.0f / lt;
-    static_assert(NW * 32 * RB <= 4 * TILE, "O staging fits the K/V buffers");
+    static_assert(NW * 32 * RB <= (2 + NVB) * TILE, "O staging fits the K/V buffers");
     unsigned char* ow = smem + wave * 32 * RB;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
