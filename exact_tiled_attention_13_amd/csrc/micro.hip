@@ -47,7 +47,8 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
 // change); MODE 1 -- eight register pairs of pseudo-random values used in
 // turn (the multiplier inputs change every product, as with real data);
 // MODE 2 -- the A operand of every product read from LDS (ds_read_b128,
-// pseudo-random contents, conflict-free), B from registers as in MODE 1.
+// pseudo-random contents, conflict-free), B from registers as in MODE 1;
+// MODE 3 -- both operands read from LDS (2 KB per product).
 template <int MODE>
 __global__ __launch_bounds__(256) void micro_mfma_bf16_kernel(float* out, unsigned long long* clk, int iters) {
     __shared__ __attribute__((aligned(16))) __bf16 lds[64 * 1024 / 2];
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void micro_mfma_bf16_kernel(float* out, unsign
             a[r][i] = MODE == 0 ? (__bf16)((float)((lane + i) & 7) * 0.125f) : rnd_bf16(seed + 16 * r + i);
             b[r][i] = MODE == 0 ? (__bf16)((float)((lane * 3 + i) & 7) * 0.0625f) : rnd_bf16(seed + 16 * r + 8 + i);
         }
-    if constexpr (MODE == 2) {
+    if constexpr (MODE >= 2) {
         for (int i = threadIdx.x; i < 64 * 1024 / 2; i += 256) lds[i] = rnd_bf16(blockIdx.x * 65536u + i);
         __syncthreads();
     }
@@ -74,8 +75,9 @@ __global__ __launch_bounds__(256) void micro_mfma_bf16_kernel(float* out, unsign
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             bf16x8 x = a[r];
-            if constexpr (MODE == 2) x = *(const lds_bf16x8_t*)(lds + lbase + ((it + r) & 15) * 512);
-            const bf16x8 y = MODE == 0 ? b[0] : b[r];
+            if constexpr (MODE >= 2) x = *(const lds_bf16x8_t*)(lds + lbase + ((it + r) & 15) * 512);
+            bf16x8 y = MODE == 0 ? b[0] : b[r];
+            if constexpr (MODE == 3) y = *(const lds_bf16x8_t*)(lds + lbase + ((it + r + 8) & 15) * 512);
             const bf16x8 xa = MODE == 0 ? a[0] : x;
             if (r % 4 == 0) c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c0, 0, 0, 0);
             if (r % 4 == 1) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c1, 0, 0, 0);
@@ -197,6 +199,8 @@ int fa_micro_mfma_bf16(float* out, unsigned long long* clk, int blocks, int iter
         hipLaunchKernelGGL(micro_mfma_bf16_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, out, clk, iters);
     else if (mode == 2)
         hipLaunchKernelGGL(micro_mfma_bf16_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, out, clk, iters);
+    else if (mode == 3)
+        hipLaunchKernelGGL(micro_mfma_bf16_kernel<3>, dim3((unsigned)blocks), dim3(256), 0, stream, out, clk, iters);
     else
         return kInvalid;
     return hipGetLastError() == hipSuccess ? kOk : kHip;

@@ -44,12 +44,14 @@ extern "C" {
  * register pair (no operand bit ever changes); 1 -- eight register pairs of
  * pseudo-random values in [-2, 2) used in turn; 2 -- as 1, but the A operand
  * of every product is read from LDS (ds_read_b128 of pseudo-random values,
- * 1 KB per product per wave). The modes separate the energy of the matrix
+ * 1 KB per product per wave); 3 -- both operands read from LDS (2 KB per
+ * product per wave: at one product per 32 clocks on all four SIMDs, 256
+ * bytes per clock per CU). The modes separate the energy of the matrix
  * cores' arithmetic from that of their operand traffic (the chip lowers its
  * clock as its power rises). out: blocks * 256 floats (one checksum per
  * thread, so that no product is dropped). clk: 4 * blocks words.
  * FLOP = blocks * 4 waves * iters * 4 * 32768. blocks >= 1, 2 <= iters <= 2^24,
- * iters even; mode in {0, 1, 2}.
+ * iters even; mode in {0, 1, 2, 3}.
  */
 int fa_micro_mfma_bf16(float* out, unsigned long long* clk, int blocks, int iters, int mode, hipStream_t stream);
 
