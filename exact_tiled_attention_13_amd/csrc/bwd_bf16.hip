@@ -412,7 +412,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 // with complementary work:
 //
 //   P wave  (w < 4):  S = Q K^T, P = exp2(S c2 - LSE2) (K rows in VGPRs),
-//                     dV^T += dO^T P; P goes to LDS in fp32 for the partner.
+//                     dV^T += dO^T P; P goes to LDS for the partner as the
+//                     bf16 pairs the dV product uses.
 //   dS wave (w >= 4): dP - D = dO V^T - D (V rows in VGPRs; the accumulator
 //                     starts at -D); one tile later, with the partner's P,
 //                     dS = P o (dP - D) and dK^T += Q^T dS.
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     constexpr int RB = T::RB;
     static_assert(MB == 2, "the schedule below is written for two 32-query blocks");
     constexpr int SST = 2 * BQ * 4;                    // statistics stage: LSE2[BQ], -D[BQ]
-    constexpr int PXG = MB * 4 * 1024;                 // P of one key group: per block, 4 rows of 1 KB
+    constexpr int PXG = MB * 2 * 1024;                 // P (bf16) of one key group: per block, 2 rows of 1 KB
     constexpr int PXB = 4 * PXG;                       // P exchange buffer (4 key groups)
     constexpr int QOFF = 0;                            // Q tiles, 3 stages
     constexpr int GOFF = 3 * T::BYTES;                 // dO tiles, 2 stages
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     auto qtile = [&](int s) { return smem + QOFF + s * T::BYTES; };
     auto gtile = [&](int s) { return smem + GOFF + s * T::BYTES; };
     auto stats = [&](int s) { return reinterpret_cast<float*>(smem + SOFF + s * SST); };
-    auto pxch = [&](int s) { return reinterpret_cast<float*>(smem + POFF + s * PXB + kg * PXG); };
+    auto pxch = [&](int s) { return reinterpret_cast<uint32_t*>(smem + POFF + s * PXB + kg * PXG); };
 
     // Only the P waves load tiles: a direct load stalls the issuing wave until
     // the memory pipeline accepts it, and the P waves have slack at the
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         const unsigned char* Qs = qtile(qs);
         const unsigned char* Gs = gtile(gs);
         const float* Ls = stats(gs);
-        float* Px = pxch(gs);
+        uint32_t* Px = pxch(gs);
         // Causal diagonal: key myk is invisible to queries before it; thr is
         // the key minus the element-0 query of the block.
         const int thr[2] = {MASKED ? myk - (q0 + 4 * hi) : 0, MASKED ? myk - (q0 + 32 + 4 * hi) : 0};
@@ -586,10 +587,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
             }
             if (k & 1) {
                 const int g4 = k >> 1;
-                const f32x4 v = {s[mb][4 * g4], s[mb][4 * g4 + 1], s[mb][4 * g4 + 2], s[mb][4 * g4 + 3]};
-                *reinterpret_cast<f32x4*>(Px + (mb * 4 + g4) * 256 + lane * 4) = v;
-                pk[mb][g4 >> 1][2 * (g4 & 1)] = pack_bf16x2(v[0], v[1]);
-                pk[mb][g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16x2(v[2], v[3]);
+                pk[mb][g4 >> 1][2 * (g4 & 1)] = pack_bf16x2(s[mb][4 * g4], s[mb][4 * g4 + 1]);
+                pk[mb][g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16x2(s[mb][4 * g4 + 2], s[mb][4 * g4 + 3]);
+                // P goes to the dS wave as the bf16 pairs dV uses: 16 bytes
+                // per lane once a group of eight is packed.
+                if (g4 & 1) *reinterpret_cast<u32x4*>(Px + (mb * 2 + (g4 >> 1)) * 256 + lane * 4) = pk[mb][g4 >> 1];
             }
         };
         bf16x8 ra[2 * DC];
@@ -651,15 +653,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         const unsigned char* Gs = gtile(gs);
         const float* Ds = stats(gs) + BQ;
         const unsigned char* Qp = qtile(qsp);
-        const float* Pp = pxch(pgs);
-        f32x4 pr[2][4];
+        const uint32_t* Pp = pxch(pgs);
+        u32x4 pr[2][2];
         u32x4 sk[2][2];
         auto ds_part = [&](int mb, int k) {
-            float v[2];
-#pragma unroll
-            for (int e = 2 * k; e < 2 * k + 2; ++e) v[e - 2 * k] = pr[mb][e >> 2][e & 3] * dp[mb][e];
-            // (elements 2k, 2k+1 form one packed word)
-            sk[mb][k >> 2][k & 3] = pack_bf16x2(v[0], v[1]);
+            // Elements 2k, 2k+1: one packed bf16 pair of P (low half first).
+            const uint32_t w = pr[mb][k >> 2][k & 3];
+            const float v0 = __uint_as_float(w << 16) * dp[mb][2 * k];
+            const float v1 = __uint_as_float(w & 0xffff0000u) * dp[mb][2 * k + 1];
+            sk[mb][k >> 2][k & 3] = pack_bf16x2(v0, v1);
         };
         bf16x8 rb[2 * DC];
         auto row_load = [&](int i) { rb[i] = T::read_row(Gs, row_off(i)); };
@@ -667,8 +669,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4)
-                    pr[mb][g4] = *reinterpret_cast<const f32x4*>(Pp + (mb * 4 + g4) * 256 + lane * 4);
+                for (int h2 = 0; h2 < 2; ++h2)
+                    pr[mb][h2] = *reinterpret_cast<const u32x4*>(Pp + (mb * 2 + h2) * 256 + lane * 4);
         }
         if (cur) {
 #pragma unroll
