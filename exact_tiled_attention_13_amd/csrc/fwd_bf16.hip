@@ -44,10 +44,11 @@ constexpr float kTau = 8.0f;
 
 // d = 128 sequences up to this length use 4-wave workgroups (see
 // fwd_bf16_kernel); d = 64 always does (measured on MI355X: 1-25% faster at
-// every length for d = 64, while for d = 128 the 8-wave form wins from 4096
-// tokens on, where the 4-wave form's larger share of tile loads per wave
-// spills registers).
-constexpr int kFwdShortN = 2048;
+// every length for d = 64). For d = 128 the 8-wave ping-pong form wins
+// beyond 1024 tokens (4-7% at 1500-2048 tokens without the mask, 7% at 1536
+// with it, 4-8% at 2730-4096); at 512-1024 tokens the two are level within
+// 2%.
+constexpr int kFwdShortN = 1024;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;

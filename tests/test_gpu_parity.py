@@ -56,10 +56,12 @@ def test_fwd_fp32_shapes(N, d, causal):
 # ---------------------------------------------------------------------------
 # bf16 forward, whole-tensor comparison
 
-@pytest.mark.parametrize("N", [1, 17, 100, 129, 257, 1000])
+@pytest.mark.parametrize("N", [1, 17, 100, 129, 257, 1000, 1024, 1025, 1537])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_bf16_shapes(N, d, causal):
+    """Whole tensors against the oracle. At d = 128, 1025 tokens and more run
+    the 8-wave ping-pong forward, 1024 and fewer the 4-wave one."""
     q, k, v = make_qkv(2, 3, N, d, "bf16", seed=N * 10 + d + causal + 7)
     s = float(np.float32(d ** -0.5))
     o, lse = run_fwd(q, k, v, causal, s)
