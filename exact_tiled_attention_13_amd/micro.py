@@ -101,12 +101,14 @@ def mfma_bf16(dev=None, blocks_per_cu: int = 4, iters: int = 40000, reps: int = 
             "cus": cus, "blocks": blocks, "iters": iters}
 
 
-def mfma_with_valu(dev=None, nfma: int = 0, nexp: int = 0, iters: int = 20000, reps: int = 3) -> dict:
+def mfma_with_valu(dev=None, nfma: int = 0, nexp: int = 0, iters: int = 20000, reps: int = 3,
+                   waves_per_simd: int = 2) -> dict:
     """MFMA rate when each MFMA of a wave is followed by `nfma` v_fma_f32 and `nexp` v_exp_f32 of its own
-    (two waves per SIMD, random operands): how much VALU work a wave can place between its MFMAs for free."""
+    (random operands; `waves_per_simd` workgroups of four waves per CU): how much VALU work a wave can place
+    between its MFMAs for free, with or without a second wave on its SIMD."""
     dev = dev or torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    blocks = cus * 2
+    blocks = cus * waves_per_simd
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     clk = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
     ms = _timed(dev, lambda: lib().fa_micro_mfma_valu(out.data_ptr(), clk.data_ptr(), blocks, iters, nfma, nexp,
@@ -115,7 +117,8 @@ def mfma_with_valu(dev=None, nfma: int = 0, nexp: int = 0, iters: int = 20000, r
     ghz = clock_ghz(clk)
     tflops = flop / ms / 1e9
     at_clock = cus * 4 * 1024 * ghz * 1e9 / 1e12
-    return {"nfma": nfma, "nexp": nexp, "tflops": round(tflops, 1), "clock_ghz": round(ghz, 3),
+    return {"nfma": nfma, "nexp": nexp, "waves_per_simd": waves_per_simd, "tflops": round(tflops, 1),
+            "clock_ghz": round(ghz, 3),
             "util_at_clock": round(tflops / at_clock, 4), "ms": round(ms, 3)}
 
 
