@@ -48,7 +48,9 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
 // turn (the multiplier inputs change every product, as with real data);
 // MODE 2 -- the A operand of every product read from LDS (ds_read_b128,
 // pseudo-random contents, conflict-free), B from registers as in MODE 1;
-// MODE 3 -- both operands read from LDS (2 KB per product).
+// MODE 3 -- both operands read from LDS (2 KB per product); MODE 4 / 5 -- as
+// MODE 1, but with one / two accumulator chains instead of four (every
+// product depends on the one issued one / two products earlier).
 template <int MODE>
 __global__ __launch_bounds__(256) void micro_mfma_bf16_kernel(float* out, unsigned long long* clk, int iters) {
     __shared__ __attribute__((aligned(16))) __bf16 lds[64 * 1024 / 2];
@@ -79,10 +81,11 @@ __global__ __launch_bounds__(256) void micro_mfma_bf16_kernel(float* out, unsign
             bf16x8 y = MODE == 0 ? b[0] : b[r];
             if constexpr (MODE == 3) y = *(const lds_bf16x8_t*)(lds + lbase + ((it + r + 8) & 15) * 512);
             const bf16x8 xa = MODE == 0 ? a[0] : x;
-            if (r % 4 == 0) c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c0, 0, 0, 0);
-            if (r % 4 == 1) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c1, 0, 0, 0);
-            if (r % 4 == 2) c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c2, 0, 0, 0);
-            if (r % 4 == 3) c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c3, 0, 0, 0);
+            constexpr int NC = MODE == 4 ? 1 : MODE == 5 ? 2 : 4;   // accumulator chains
+            if (r % NC == 0) c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c0, 0, 0, 0);
+            if (r % NC == 1) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c1, 0, 0, 0);
+            if (r % NC == 2) c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c2, 0, 0, 0);
+            if (r % NC == 3) c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, y, c3, 0, 0, 0);
         }
     }
     stamp_end(clk, t0, r0);
@@ -201,6 +204,10 @@ int fa_micro_mfma_bf16(float* out, unsigned long long* clk, int blocks, int iter
         hipLaunchKernelGGL(micro_mfma_bf16_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, out, clk, iters);
     else if (mode == 3)
         hipLaunchKernelGGL(micro_mfma_bf16_kernel<3>, dim3((unsigned)blocks), dim3(256), 0, stream, out, clk, iters);
+    else if (mode == 4)
+        hipLaunchKernelGGL(micro_mfma_bf16_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, out, clk, iters);
+    else if (mode == 5)
+        hipLaunchKernelGGL(micro_mfma_bf16_kernel<5>, dim3((unsigned)blocks), dim3(256), 0, stream, out, clk, iters);
     else
         return kInvalid;
     return hipGetLastError() == hipSuccess ? kOk : kHip;

@@ -84,7 +84,7 @@ def mfma_bf16(dev=None, blocks_per_cu: int = 4, iters: int = 40000, reps: int = 
     at one MFMA per 32 clocks per SIMD (MI355X's 1024 dense bf16 FLOP per clock per SIMD). `mode` picks the
     operand source (include/fa_micro.h): 0 constant registers, 1 changing pseudo-random registers,
     2 the A operand from LDS, 3 both operands from LDS (the LDS modes hold 64 KB per workgroup, so two
-    workgroups share a CU: two waves per SIMD)."""
+    workgroups share a CU: two waves per SIMD), 4 / 5 as 1 with one / two accumulator chains per wave."""
     dev = dev or torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     blocks = cus * blocks_per_cu
@@ -161,7 +161,7 @@ def atomic_add(dev=None, n: int = 1 << 26, reps: int = 4) -> dict:
 
 def main():
     dev = torch.device("cuda:0")
-    res = {f"mfma_bf16_mode{m}": mfma_bf16(dev, mode=m) for m in (0, 1, 2, 3)}
+    res = {f"mfma_bf16_mode{m}": mfma_bf16(dev, mode=m) for m in (0, 1, 2, 3, 4, 5)}
     res.update({"exp2": exp2_rate(dev), "atomic_add_f32": atomic_add(dev)})
     res["mfma_with_valu"] = [mfma_with_valu(dev, f, e) for f, e in ((0, 0), (2, 0), (4, 0), (8, 0), (0, 1), (0, 2),
                                                                     (0, 4), (4, 2), (6, 2))]

@@ -46,12 +46,14 @@ extern "C" {
  * of every product is read from LDS (ds_read_b128 of pseudo-random values,
  * 1 KB per product per wave); 3 -- both operands read from LDS (2 KB per
  * product per wave: at one product per 32 clocks on all four SIMDs, 256
- * bytes per clock per CU). The modes separate the energy of the matrix
+ * bytes per clock per CU); 4 and 5 -- as 1, with one and two accumulator
+ * chains instead of four (each product depends on the one issued one or two
+ * products earlier). The modes separate the energy of the matrix
  * cores' arithmetic from that of their operand traffic (the chip lowers its
  * clock as its power rises). out: blocks * 256 floats (one checksum per
  * thread, so that no product is dropped). clk: 4 * blocks words.
  * FLOP = blocks * 4 waves * iters * 4 * 32768. blocks >= 1, 2 <= iters <= 2^24,
- * iters even; mode in {0, 1, 2, 3}.
+ * iters even; mode in {0, ..., 5}.
  */
 int fa_micro_mfma_bf16(float* out, unsigned long long* clk, int blocks, int iters, int mode, hipStream_t stream);
 

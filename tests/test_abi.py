@@ -81,7 +81,7 @@ def test_micro_rejects_bad_arguments():
     L = micro.lib()
     assert L.fa_micro_mfma_bf16(0, P, 4, 2, 0, None) == 1
     assert L.fa_micro_mfma_bf16(P, P, 4, 3, 0, None) == 1       # odd iteration count
-    assert L.fa_micro_mfma_bf16(P, P, 4, 2, 4, None) == 1       # unknown operand mode
+    assert L.fa_micro_mfma_bf16(P, P, 4, 2, 6, None) == 1       # unknown operand mode
     assert L.fa_micro_exp2(P, P, 0, 1, None) == 1
     assert L.fa_micro_mfma_valu(P, P, 4, 10, 3, 0, None) == 1   # unsupported mix
     assert L.fa_micro_fp8_dot(P, P, P, 1, 65, None) == 1
