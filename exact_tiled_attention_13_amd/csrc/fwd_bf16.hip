@@ -42,6 +42,18 @@ namespace fa {
 // exact softmax, with the rescale of l and O skipped for most tiles.
 constexpr float kTau = 8.0f;
 
+// In the 8-wave form a tile's exponentials are taken against the running
+// maximum m before the tile's own maximum is known. While every partial row sum of a tile (one
+// lane's 32 keys) stays at or below kSumLimit, every probability is at most
+// kSumLimit, far inside fp32 and bf16 range, and m stays. A partial sum
+// above the limit (or not finite) sends the wave through the rescale path:
+// the tile's scores are formed again (from K in global memory; the tile's
+// LDS buffer is already being refilled), m moves to their maximum, l and O
+// are rescaled, and the tile's probabilities are taken again. Which m is
+// used changes no result but rounding: O / l and LSE = m + log2(l) are the
+// same exact softmax. The first tile's maximum is taken before the loop.
+constexpr float kSumLimit = 65536.0f;
+
 // d = 128 sequences up to this length use 4-wave workgroups (see
 // fwd_bf16_kernel); d = 64 always does (measured on MI355X: 1-25% faster at
 // every length for d = 64). For d = 128 the 8-wave ping-pong form wins
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     // Masking (tiles straddling the causal diagonal or the ragged end only:
     // masked scores become -inf; c2 > 0, so their exponentials are exactly
     // 0), row maximum and the lazy rescale of l and O for tile t in s.
-    auto prepare = [&](int t, f32x16 (&s)[KB], auto masked_c) {
+    auto apply_mask = [&](int t, f32x16 (&s)[KB], auto masked_c) {
         if constexpr (decltype(masked_c)::value) {
             // Key of element u of block kb is j0 + kb*32 + 4*hi + 8*(u/4) + u%4.
             const int lim = CAUSAL ? min(N - 1, myq) : N - 1;   // last visible key
@@ -296,6 +308,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
                 for (int u = 0; u < 16; ++u) s[kb][u] = (8 * (u >> 2) + (u & 3) > thr) ? -INFINITY : s[kb][u];
             }
         }
+    };
+    auto rescale_to_max = [&](f32x16 (&s)[KB]) {
         // Four independent max chains instead of one serial chain.
         float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -314,6 +328,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         }
+    };
+    auto prepare = [&](int t, f32x16 (&s)[KB], auto masked_c) {
+        apply_mask(t, s, masked_c);
+        rescale_to_max(s);
     };
 
     // One pipeline step, scheduled by hand (sched_barrier fences keep the
@@ -352,7 +370,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
 #pragma unroll
         for (int i = 0; i < KBS; ++i) kfr[i] = kread(i);
         fence();
-        prepare(t, scur, masked_c);
+        // The 8-wave form defers the tile maximum to the rare rescale path
+        // (kSumLimit); the others have no registers for that path and take
+        // the maximum first.
+        if constexpr (PP)
+            apply_mask(t, scur, masked_c);
+        else
+            prepare(t, scur, masked_c);
         fence();
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) snext[kb] = f32x16{};
@@ -417,7 +441,39 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
             valu_slot(i);
             fence();
         }
-        l += rsum[0] + rsum[1];
+        float tsum = rsum[0] + rsum[1];
+        if (PP && __builtin_amdgcn_ballot_w64(!(tsum <= kSumLimit)) != 0) {
+            // Rare: somewhere in the wave this tile's maximum exceeds the
+            // running one by more than log2(kSumLimit / 32).
+            f32x16 sr[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                sr[kb] = f32x16{};
+                const int krow = min(t * BN + kb * 32 + l32, N - 1);   // rows past N are masked
+#pragma unroll
+                for (int cc = 0; cc < DC; ++cc) {
+                    // One operand at a time: this path is rare, its registers are not.
+                    const bf16x8 kf = as_bf16x8(ld16(Kg + (size_t)krow * rskv + cc * 16 + hi * 8));
+                    sr[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cc], sr[kb], 0, 0, 0);
+                    fence();
+                }
+            }
+            apply_mask(t, sr, masked_c);
+            rescale_to_max(sr);
+            fence();
+            tsum = 0.f;
+#pragma unroll
+            for (int q = 0; q < NPAIR; ++q) {
+                const int f = 2 * q, kb = f / 16, u = f % 16;
+                const float e0 = exp2_fast(__builtin_fmaf(sr[kb][u], c2, -m));
+                const float e1 = exp2_fast(__builtin_fmaf(sr[kb][u + 1], c2, -m));
+                tsum += e0 + e1;
+                w[f / 8][(f % 8) / 2] = pack_bf16x2(e0, e1);
+                if (f % 8 == 6) pb[f / 8] = as_bf16x8(w[f / 8]);
+                fence();
+            }
+        }
+        l += tsum;
         if (lag) {
             // A lagging wave's barrier: phase A of tile t is done, phase B
             // follows in the next interval.
@@ -480,6 +536,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     // workgroup's first query and before N); the rest run the masked variant.
     // Causal waves whose rows all precede a tile run it fully masked (p = 0).
     const int t_split = min(CAUSAL ? q0 / BN : ntiles, (N % BN) ? ntiles - 1 : ntiles);
+    // The running maximum starts at the first tile's (every row sees key 0).
+    if constexpr (PP) {
+        if (t_split > 0)
+            prepare(0, sa, std::false_type{});
+        else
+            prepare(0, sa, std::true_type{});
+    }
+
     // Step t runs with S_t in sa when t is even, in sb when odd.
     auto run = [&](int t, auto r_c, auto masked_c) {
         if constexpr (decltype(r_c)::value & 1)

@@ -70,6 +70,25 @@ def test_fwd_bf16_shapes(N, d, causal):
     assert aerr(f64(lse), rl) <= TOL_LSE_BF16
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_bf16_rising_scores(causal):
+    """Scores that rise by about 16 (base 2) from each 64-key tile to the next: the 8-wave forward
+    (1100 tokens at d = 128) takes every tile's exponentials against a running maximum that the tile
+    then exceeds, so every tile goes through its rescale path (scores formed again, maximum moved, l
+    and O rescaled)."""
+    N, d = 1100, 128
+    g = torch.Generator().manual_seed(5101 + causal)
+    q = (0.1 + 0.02 * torch.randn(1, N, 2, d, generator=g)).to(torch.bfloat16)
+    ramp = (10.0 * (torch.arange(N) // 64)).view(1, N, 1, 1)
+    k = (ramp + torch.randn(1, N, 2, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(1, N, 2, d, generator=g).to(torch.bfloat16)
+    s = float(np.float32(d ** -0.5))
+    o, lse = run_fwd(q, k, v, causal, s)
+    ro, rl = attn_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, s)
+    assert nerr(f64(o), ro) <= TOL_O_BF16
+    assert aerr(f64(lse), rl) <= TOL_LSE_BF16
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_bf16_other_scales(scale, causal):
