@@ -20,6 +20,9 @@
 //                 accumulator each lane holds one query column (lane % 32) and
 //                 16 keys, so the row max / row sum are in-lane plus one
 //                 exchange with lane ^ 32.
+//   In the 8-wave form (d = 128 beyond 1024 tokens) waves 4-7 run half a step
+//   behind waves 0-3 (ping-pong), and a tile's row maximum is only taken when
+//   its probabilities outgrow the running one (kSumLimit below).
 //   O^T += V^T P^T  A = V^T tile from LDS (stored transposed, keys permuted
 //                 within 16-key chunks to the order the accumulator holds
 //                 them in), B = P^T converted in registers from the S^T
@@ -43,9 +46,10 @@ namespace fa {
 constexpr float kTau = 8.0f;
 
 // In the 8-wave form a tile's exponentials are taken against the running
-// maximum m before the tile's own maximum is known. While every partial row sum of a tile (one
-// lane's 32 keys) stays at or below kSumLimit, every probability is at most
-// kSumLimit, far inside fp32 and bf16 range, and m stays. A partial sum
+// maximum m before the tile's own maximum is known. While every partial row
+// sum of a tile (one lane's 32 keys) stays at or below kSumLimit, every
+// probability is at most kSumLimit, far inside fp32 and bf16 range, and m
+// stays. A partial sum
 // above the limit (or not finite) sends the wave through the rescale path:
 // the tile's scores are formed again (from K in global memory; the tile's
 // LDS buffer is already being refilled), m moves to their maximum, l and O
