@@ -304,15 +304,17 @@ def main():
     names = []
     for c in masks:
         tag = "causal" if c else "noncausal"
-        names += [f"fwd_{tag}", f"bwd_prep_{tag}", f"bwd_dkdv_{tag}", f"bwd_dq_{tag}"]
+        names += [f"fwd_{tag}", f"bwd_dq_prep_{tag}", f"bwd_dkdv_{tag}"]
 
+    # The backward as attn_bwd runs it: dQ with the row statistics formed in
+    # its kernel (attn_bwd_dq_prep), then dK/dV.
     def launches(c):
         b = bufs[c]
         return [
             lambda: fa.attn_fwd(qd, kd, vd, c, scale, o=b["o"], lse=b["lse"]),
-            lambda: fa.attn_bwd_prep(b["o"], dod, b["lse"], ws=b["ws"]),
+            lambda: fa.attn_bwd_dq_prep(qd, kd, vd, b["o"], dod, b["lse"], ws=b["ws"], causal=c, scale=scale,
+                                        dq=b["dq"]),
             lambda: fa.attn_bwd_dkdv(qd, kd, vd, dod, b["ws"], c, scale, dk=b["dk"], dv=b["dv"]),
-            lambda: fa.attn_bwd_dq(qd, kd, vd, dod, b["ws"], c, scale, dq=b["dq"]),
         ]
 
     calls = [f for c in masks for f in launches(c)]
@@ -354,8 +356,7 @@ def main():
         f1 = counted_fwd(B, H, N, d, c) / 2           # one N x N x d product
         work[f"fwd_{tag}"] = ("mfma", 2 * f1)
         work[f"bwd_dkdv_{tag}"] = ("mfma", 4 * f1)     # S (recompute), dP, dV, dK
-        work[f"bwd_dq_{tag}"] = ("mfma", 1 * f1)       # dQ (S, dP recomputed again: not counted)
-        work[f"bwd_prep_{tag}"] = ("hbm", 2.0 * B * N * H * d * 2 + 4.0 * B * H * N + 8.0 * B * H * N)
+        work[f"bwd_dq_prep_{tag}"] = ("mfma", 1 * f1)  # dQ (S, dP recomputed again: not counted)
     step_flops = sum(counted_fwd(B, H, N, d, c) * 3.5 for c in masks)
 
     breakdown = {}
@@ -375,7 +376,7 @@ def main():
     for c in masks:
         tag = "causal" if c else "noncausal"
         fms = kern_ms[f"fwd_{tag}"]
-        bms = kern_ms[f"bwd_prep_{tag}"] + kern_ms[f"bwd_dkdv_{tag}"] + kern_ms[f"bwd_dq_{tag}"]
+        bms = kern_ms[f"bwd_dq_prep_{tag}"] + kern_ms[f"bwd_dkdv_{tag}"]
         ff = counted_fwd(B, H, N, d, c)
         passes[f"fwd_{tag}"] = {"ms": round(fms, 4), "tflops": round(ff / fms / 1e9, 1),
                                 "frac_bf16_peak": round(ff / fms / 1e9 / PEAK_BF16_TFLOPS, 4)}

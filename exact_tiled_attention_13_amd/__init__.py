@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     attn_bwd,
     attn_bwd_dkdv,
     attn_bwd_dq,
+    attn_bwd_dq_prep,
     attn_bwd_gqa,
     attn_bwd_gqa_workspace_size,
     attn_bwd_noalloc,

@@ -30,7 +30,7 @@ FA_ERR_WORKSPACE = 3
 FA_ERR_HIP = 4
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_prep",
-            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_size",
+            "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_prep", "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_size",
             "attn_decode_workspace_size",
             "attn_decode", "attn_fwd_fp8", "attn_bwd_noalloc", "fa_status_string")
 
@@ -94,6 +94,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.attn_bwd_dkdv.restype = ci
     L.attn_bwd_dq.argtypes = [vp] * 5 + [sz, vp, ci, ci, ci, ci, ci, cf, vp]
     L.attn_bwd_dq.restype = ci
+    L.attn_bwd_dq_prep.argtypes = [vp] * 7 + [sz, vp, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_bwd_dq_prep.restype = ci
     L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
     L.attn_fwd_gqa.restype = ci
     L.attn_bwd_gqa.argtypes = [vp] * 9 + [vp, sz] + [ci, ci, ci, ci, ci, ci, cf, vp]
@@ -294,6 +296,23 @@ def attn_bwd_dq(q, k, v, do, ws, causal: bool = False, scale: float | None = Non
     _check("attn_bwd_dq", lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(ws), _nbytes(ws), _ptr(dq),
                                             B, H, N, d, int(bool(causal)), s, _stream(dev)))
     return dq
+
+
+def attn_bwd_dq_prep(q, k, v, o, do, lse, ws=None, causal: bool = False, scale: float | None = None, dq=None):
+    """dQ, and the workspace's row statistics for attn_bwd_dkdv, in one launch (attn_bwd_prep's work fused
+    into attn_bwd_dq). Returns (dq, ws)."""
+    B, N, H, d = _shape(q)
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq)):
+        _expect(name, t, (B, N, H, d), torch.bfloat16, dev)
+    _expect("lse", lse, (B, H, N), torch.float32, dev)
+    ws = workspace(B, H, N, d, dev) if ws is None else ws
+    s = default_scale(d) if scale is None else float(scale)
+    _check("attn_bwd_dq_prep", lib().attn_bwd_dq_prep(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                                      _ptr(ws), _nbytes(ws), _ptr(dq), B, H, N, d,
+                                                      int(bool(causal)), s, _stream(dev)))
+    return dq, ws
 
 
 def _kv_heads(q, k):

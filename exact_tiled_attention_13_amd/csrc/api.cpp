@@ -198,16 +198,20 @@ int dkdv_stage(const void* q, const void* k, const void* v, const void* dO, cons
     return fa::launch_bwd_dkdv(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int dq_stage(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
-             size_t workspace_bytes, void* dq, int B, int H, int Hkv, int N, int d, int causal, float scale,
-             hipStream_t stream) {
+// o and lse non-null: the fused form that also fills the workspace's statistics.
+int dq_stage(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             const void* workspace, size_t workspace_bytes, void* dq, int B, int H, int Hkv, int N, int d,
+             int causal, float scale, hipStream_t stream) {
     fa::BwdArgs a{};
     int st = fill_bwd(a, q, k, v, dO, workspace, workspace_bytes, B, H, Hkv, N, d, scale);
     if (st != FA_OK) return st;
-    st = check_ptrs({dq});
+    const bool prep = o != nullptr || lse != nullptr;
+    st = prep ? check_ptrs({dq, o, lse}) : check_ptrs({dq});
     if (st != FA_OK) return st;
     a.dq = dq;
-    return fa::launch_bwd_dq(a, d, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    a.o = o;
+    a.lse = lse;
+    return fa::launch_bwd_dq(a, d, causal != 0, prep, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // namespace
@@ -223,7 +227,15 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, c
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
                 size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal, float scale,
                 hipStream_t stream) {
-    return dq_stage(q, k, v, dO, workspace, workspace_bytes, dq, B, H, H, N, d, causal, scale, stream);
+    return dq_stage(q, k, v, nullptr, dO, nullptr, workspace, workspace_bytes, dq, B, H, H, N, d, causal, scale,
+                    stream);
+}
+
+int attn_bwd_dq_prep(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                     void* workspace, size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal,
+                     float scale, hipStream_t stream) {
+    if (o == nullptr || lse == nullptr) return FA_ERR_INVALID_ARG;
+    return dq_stage(q, k, v, o, dO, lse, workspace, workspace_bytes, dq, B, H, H, N, d, causal, scale, stream);
 }
 
 size_t attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d, int causal) {
@@ -243,11 +255,10 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
     if (st != FA_OK) return st;
     st = check_ws(workspace, workspace_bytes, B, H, N);
     if (st != FA_OK) return st;
-    st = attn_bwd_prep(o, dO, lse, workspace, workspace_bytes, B, H, N, d, stream);
+    // dQ first: its kernel also writes the row statistics the dK/dV kernel reads.
+    st = dq_stage(q, k, v, o, dO, lse, workspace, workspace_bytes, dq, B, H, Hkv, N, d, causal, scale, stream);
     if (st != FA_OK) return st;
-    st = dkdv_stage(q, k, v, dO, workspace, workspace_bytes, dk, dv, B, H, Hkv, N, d, causal, scale, stream);
-    if (st != FA_OK) return st;
-    return dq_stage(q, k, v, dO, workspace, workspace_bytes, dq, B, H, Hkv, N, d, causal, scale, stream);
+    return dkdv_stage(q, k, v, dO, workspace, workspace_bytes, dk, dv, B, H, Hkv, N, d, causal, scale, stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

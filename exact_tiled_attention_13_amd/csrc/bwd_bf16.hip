@@ -7,7 +7,7 @@
 // softmax, with P recomputed tile by tile from Q, K and the forward's LSE so
 // that no N x N matrix is stored:
 //
-//     D_i = dO_i . O_i                      (kernel bwd_pre)
+//     D_i = dO_i . O_i                      (kernel bwd_pre, or bwd_dq with PREP)
 //     P   = exp(scale * Q K^T - LSE)         (masked entries 0)
 //     dV  = P^T dO,  dP = dO V^T,  dS = P o (dP - D)
 //     dK  = scale * dS^T Q                  (kernel bwd_dkdv: key-block outer)
@@ -810,7 +810,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 // staged in LDS by direct loads, double-buffered. S^T = K Q^T and dP^T = V dO^T use row reads of the K and V
 // tiles; dQ^T += K^T dS^T takes its A operand from transposing reads of the
 // same K tile. The accumulators hold one query per lane, as in the forward.
-template <int D, bool CAUSAL, int NW>
+//
+// PREP: the kernel also does bwd_pre's work for its own queries. Each lane
+// already holds half of its query's dO row; it loads the same half of the O
+// row and forms -D and LSE * log2(e) in registers, and writes both into the
+// workspace for the dK/dV kernel, which then runs after this one. The dot
+// product is summed in exactly bwd_pre's order (8 products per 16-byte
+// chunk, then the chunks pairwise as its butterfly over 16 threads pairs
+// them), so the statistics, and with them dQ, dK and dV, are bitwise those of
+// the separate preprocess.
+template <int D, bool CAUSAL, int NW, bool PREP>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     using T = LdsTile<D>;
     constexpr int BM = NW * 32;          // queries per workgroup
@@ -853,6 +862,15 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void bwd_dq_kernel(B
     const int myq = qw + l32;
 
     bf16x8 qf[DC], gf[DC];
+    // PREP: this lane's half of its O row. Loaded for every lane (rows past
+    // the end read row N - 1, and their statistics are discarded below), so
+    // that no wait for these loads is needed before the first tile's loads.
+    u32x4 orow[PREP ? DC : 1];
+    if constexpr (PREP) {
+        const __bf16* Or = static_cast<const __bf16*>(a.o) + base + (size_t)min(myq, N - 1) * rs + hi * 8;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) orow[c] = ld16(Or + c * 16);
+    }
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
         u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
@@ -864,8 +882,46 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void bwd_dq_kernel(B
         qf[c] = as_bf16x8(qv);
         gf[c] = as_bf16x8(gv);
     }
-    const float lse2 = (myq < N) ? a.lse2[(size_t)bh * npad + myq] : 0.f;
-    const float ndd = (myq < N) ? a.dd[(size_t)bh * npad + myq] : 0.f;   // -D of this lane's query
+    float lse2 = 0.f, ndd = 0.f;         // LSE * log2(e) and -D of this lane's query
+    float lse_in = 0.f;
+    if constexpr (PREP) {
+        lse_in = a.lse[(size_t)bh * N + min(myq, N - 1)];   // discarded past the end, as the O row
+    } else {
+        lse2 = (myq < N) ? a.lse2[(size_t)bh * npad + myq] : 0.f;
+        ndd = (myq < N) ? a.dd[(size_t)bh * npad + myq] : 0.f;
+    }
+    // PREP, once the first K/V tile's loads are in flight (so that the wait
+    // for the O rows does not delay them): -D and LSE * log2(e), written to
+    // the workspace by the lanes of the lower half.
+    auto preprocess = [&] {
+        float part[DC];                  // dO . O over each 16-byte chunk of the row
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const u32x4 ov = orow[c];
+            const u32x4 gv = as_u32x4(gf[c]);
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc += __uint_as_float(ov[w] << 16) * __uint_as_float(gv[w] << 16);
+                acc += __uint_as_float(ov[w] & 0xffff0000u) * __uint_as_float(gv[w] & 0xffff0000u);
+            }
+            part[c] = acc;
+        }
+        // Chunk j = 2c + hi of the row; bwd_pre's butterfly adds chunks j ^ 8,
+        // then j ^ 4, j ^ 2 and j ^ 1: c ^ (DC/2) ... c ^ 1 here, then the halves.
+#pragma unroll
+        for (int w = DC / 2; w > 0; w >>= 1)
+#pragma unroll
+            for (int c = 0; c < w; ++c) part[c] = part[c] + part[c + w];
+        const float dsum = sum_halves(part[0]);
+        lse2 = (myq < N) ? lse_in * kLog2e : 0.f;
+        ndd = (myq < N) ? -dsum : 0.f;
+        if (hi == 0 && myq < npad) {
+            const size_t i = (size_t)bh * npad + myq;
+            a.dd[i] = ndd;
+            a.lse2[i] = (myq < N) ? lse2 : INFINITY;
+        }
+    };
 
     f32x16 dqacc[DB];
 #pragma unroll
@@ -961,6 +1017,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void bwd_dq_kernel(B
     // variant. The split keeps mask arithmetic out of the main loop.
     const int t_split = min(CAUSAL ? q0 / BN : ntiles, (N % BN) ? ntiles - 1 : ntiles);
     dma(0, 0);
+    if constexpr (PREP) preprocess();
     wait_dma();
     __syncthreads();
     for (int t = 0; t < t_split; ++t) {
@@ -1046,7 +1103,7 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PREP>
 static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
     // 4-wave workgroups (two per CU at d = 128, three at d = 64) for d = 64
     // and for d = 128 up to 2048 tokens, as in the forward (measured: 5-26%
@@ -1054,12 +1111,12 @@ static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
     if constexpr (D == 128) {
         if (a.N > 2048) {
             const long long g = (long long)((a.N + 255) / 256) * a.B * a.H;
-            hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 8>), dim3((unsigned)g), dim3(512), 0, stream, a);
+            hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 8, PREP>), dim3((unsigned)g), dim3(512), 0, stream, a);
             return hipGetLastError();
         }
     }
     const long long g = (long long)((a.N + 127) / 128) * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 4>), dim3((unsigned)g), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 4, PREP>), dim3((unsigned)g), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1072,9 +1129,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t str
     return causal ? launch_dkdv<64, true>(a, stream) : launch_dkdv<64, false>(a, stream);
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
-    if (d == 128) return causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
-    return causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, bool prep, hipStream_t stream) {
+    if (prep) {
+        if (d == 128) return causal ? launch_dq<128, true, true>(a, stream) : launch_dq<128, false, true>(a, stream);
+        return causal ? launch_dq<64, true, true>(a, stream) : launch_dq<64, false, true>(a, stream);
+    }
+    if (d == 128) return causal ? launch_dq<128, true, false>(a, stream) : launch_dq<128, false, false>(a, stream);
+    return causal ? launch_dq<64, true, false>(a, stream) : launch_dq<64, false, false>(a, stream);
 }
 
 }  // namespace fa

@@ -193,6 +193,7 @@ __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*
 __device__ __forceinline__ void st16f(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 
 // Transpose four 8-element bf16 rows (keys r0..r3, 8 consecutive d each) into
 // eight 4-element columns: out[c] holds (r0[c], r1[c], r2[c], r3[c]) as two

@@ -23,7 +23,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t str
 hipError_t launch_fwd_fp32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_prep(const BwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t stream);
-hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+// prep: the dQ kernel also computes the row statistics bwd_prep would (from
+// a.o, a.dO, a.lse) and writes them to a.dd / a.lse2 for the dK/dV kernel.
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, bool prep, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int d, bool causal, hipStream_t stream);
 // Split kernel over (chunk, K/V head, batch), then the merge over query rows.
 hipError_t launch_decode(const DecodeArgs& a, int d, bool causal, hipStream_t stream);

@@ -1,7 +1,9 @@
 """Run one stage of the attention path a few times, for profilers.
 
 Usage: python -m exact_tiled_attention_13_amd.profile_run WHAT [--causal] [--reps R]
-WHAT is one of fwd, bwd_prep, bwd_dkdv, bwd_dq, step (all four), fp8, decode,
+WHAT is one of fwd, bwd_prep, bwd_dq, bwd_dq_prep (dQ with the preprocess
+fused, as attn_bwd runs it), bwd_dkdv, step (fwd, bwd_dq_prep, bwd_dkdv: one
+forward and backward as bench.py times them), fp8, decode,
 or copy (a plain device-to-device copy of 256 MiB through torch, used to
 calibrate the HBM byte counters: it reads and writes exactly 256 MiB per
 launch).
@@ -21,7 +23,8 @@ if ROOT not in sys.path:
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq", "step", "fp8", "decode", "copy"])
+    ap.add_argument("what", choices=["fwd", "bwd_prep", "bwd_dq", "bwd_dq_prep", "bwd_dkdv", "step", "fp8",
+                                        "decode", "copy"])
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--reps", type=int, default=3)
     args = ap.parse_args()
@@ -78,12 +81,14 @@ def main():
     for _ in range(args.reps):
         if args.what in ("fwd", "step"):
             fa.attn_fwd(q, k, v, c, w.scale, o=o, lse=lse)
-        if args.what in ("bwd_prep", "step"):
+        if args.what == "bwd_prep":
             fa.attn_bwd_prep(o, do, lse, ws=ws)
+        if args.what == "bwd_dq":
+            fa.attn_bwd_dq(q, k, v, do, ws, c, w.scale, dq=dq)
+        if args.what in ("bwd_dq_prep", "step"):
+            fa.attn_bwd_dq_prep(q, k, v, o, do, lse, ws=ws, causal=c, scale=w.scale, dq=dq)
         if args.what in ("bwd_dkdv", "step"):
             fa.attn_bwd_dkdv(q, k, v, do, ws, c, w.scale, dk=dk, dv=dv)
-        if args.what in ("bwd_dq", "step"):
-            fa.attn_bwd_dq(q, k, v, do, ws, c, w.scale, dq=dq)
     torch.cuda.synchronize()
     print(f"{args.what} causal={c} done", flush=True)
 

@@ -158,9 +158,11 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
 size_t attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d, int causal);
 
 /*
- * The three stages attn_bwd runs, in order, on one stream. They are exported
- * so that a caller can time or schedule them separately; attn_bwd is exactly
- * attn_bwd_prep, then attn_bwd_dkdv, then attn_bwd_dq on the same workspace.
+ * The stages of the backward, exported so that a caller can time or schedule
+ * them separately. attn_bwd is exactly attn_bwd_dq_prep, then attn_bwd_dkdv,
+ * on one stream and one workspace. attn_bwd_prep followed by attn_bwd_dq is
+ * the same first stage in two launches: it leaves bitwise the same workspace
+ * and dq (the fused kernel sums D_i in the same order).
  *
  * attn_bwd_prep -- fills the workspace: -D_i, where D_i = sum_c dO[b, i, h, c] *
  *   O[b, i, h, c] (the row statistic sum_j P_ij dP_ij of the softmax
@@ -171,6 +173,10 @@ size_t attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d, int caus
  * attn_bwd_dq -- dq = scale * dS K: one workgroup per block of 256 queries
  *   (128 for d = 64 or N <= 2048), looping over key tiles (recomputes P and
  *   dP); reads the workspace.
+ * attn_bwd_dq_prep -- attn_bwd_dq that also does attn_bwd_prep's work: each
+ *   lane forms -D and LSE * log2(e) of its own query from the dO row it holds
+ *   and the O row, uses them, and writes them into the workspace for
+ *   attn_bwd_dkdv. o and lse as for attn_bwd (FA_ERR_INVALID_ARG if null).
  * Arguments and errors as for attn_bwd.
  */
 int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace, size_t workspace_bytes,
@@ -181,6 +187,9 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, c
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
                 size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal, float scale,
                 hipStream_t stream);
+int attn_bwd_dq_prep(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* workspace, size_t workspace_bytes, void* dq,
+                     int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
  * attn_fwd_fp8 -- FP8 (OCP E4M3) forward (page "FlashAttention-T: Optimización

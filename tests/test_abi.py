@@ -168,6 +168,15 @@ def test_backward_stages_reject_bad_arguments():
     assert L.attn_bwd_dq(P, P, P, P, P, need, 0, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
     assert L.attn_bwd_dq(P, P, P, P, 0, need, P, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_WORKSPACE
     assert L.attn_bwd_dq(P, P, P, P, P, need, P, 1, 0, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    # attn_bwd_dq_prep(q, k, v, o, dO, lse, ws, ws_bytes, dq, B, H, N, d, causal, scale, stream)
+    assert L.attn_bwd_dq_prep(P, P, P, 0, P, P, P, need, P, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_dq_prep(P, P, P, P, P, 0, P, need, P, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_dq_prep(P, P, P, P, P, MIS, P, need, P, 1, 1, 16, 64, 0, 0.125, None) \
+        == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_dq_prep(P, P, P, P, P, P, P, need, 0, 1, 1, 16, 64, 0, 0.125, None) == fa.FA_ERR_INVALID_ARG
+    assert L.attn_bwd_dq_prep(P, P, P, P, P, P, P, need - 1, P, 1, 1, 16, 64, 0, 0.125, None) \
+        == fa.FA_ERR_WORKSPACE
+    assert L.attn_bwd_dq_prep(P, P, P, P, P, P, P, need, P, 1, 1, 16, 48, 0, 0.125, None) == fa.FA_ERR_UNSUPPORTED
 
 
 @no_gpu_only
