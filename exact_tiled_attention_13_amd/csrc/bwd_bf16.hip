@@ -551,9 +551,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     // keep the compiler from regrouping the hand-placed stream.
     constexpr int PF = 3;
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    constexpr int NJ = 2 * 2 * DB;       // MFMAs of the dV (or dK) phase
+    // MFMAs of the dV (or dK) phase: step j covers block j / (2 DB), 16-query
+    // half (j / DB) % 2 and d block j % DB, so consecutive products update
+    // different accumulators (each accumulator still sums in the same order).
+    constexpr int NJ = 2 * 2 * DB;
     auto tr_off = [&](int j, int& o0, int& o1) {
-        const int mb = j / (2 * DB), db = (j / 2) % DB, half = j % 2;
+        const int mb = j / (2 * DB), half = (j / DB) % 2, db = j % DB;
         const int qc = mb * 2 + half;
         o0 = (trb0 ^ (db << 6)) + qc * 16 * RB;
         o1 = (trb1 ^ (db << 6)) + qc * 16 * RB;
@@ -630,7 +633,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         fence();
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int mb = j / (2 * DB), db = (j / 2) % DB, half = j % 2;
+            const int mb = j / (2 * DB), half = (j / DB) % 2, db = j % DB;
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j], as_bf16x8(pk[mb][half]), acc[db], 0, 0, 0);
             if (j + PF < NJ) tr_load(j + PF);
             if (mb == 0) {
@@ -721,7 +724,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
             fence();
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int mb = j / (2 * DB), db = (j / 2) % DB, half = j % 2;
+                const int mb = j / (2 * DB), half = (j / DB) % 2, db = j % DB;
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[j], as_bf16x8(sk[mb][half]), acc[db], 0, 0, 0);
                 if (j + PF < NJ) tr_load(j + PF);
                 fence();
