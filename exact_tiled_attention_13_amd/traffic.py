@@ -3,8 +3,9 @@
 Usage: python -m exact_tiled_attention_13_amd.traffic PROF_DIR [--out profiles/hbm_traffic.json]
 
 PROF_DIR holds one rocprofv3 ``--pmc`` run per stage and counter, in
-directories ``pmc_<stage>_<COUNTER>`` (stage: copy, fwd, bwd_prep, bwd_dkdv,
-bwd_dq; counter: FETCH_SIZE, WRITE_SIZE), each made by
+directories ``pmc_<stage>_<COUNTER>`` (stage: copy, fwd, bwd_dq_prep,
+bwd_dkdv -- the kernels bench.py times; counter: FETCH_SIZE, WRITE_SIZE), each
+made by
 
     rocprofv3 --pmc <COUNTER> --output-format csv -d PROF_DIR/pmc_<stage>_<COUNTER> -o run -- \\
         python3 -m exact_tiled_attention_13_amd.profile_run <stage> --reps 3
@@ -34,9 +35,8 @@ COPY_KIB = 262144
 # Stage -> (kernel name prefix in the trace, name used by bench.py).
 STAGES = {
     "fwd": ("fa::fwd_bf16_kernel<128, false, 8>", "fwd_noncausal"),
-    "bwd_prep": ("fa::bwd_pre_kernel<128>", "bwd_prep_noncausal"),
+    "bwd_dq_prep": ("fa::bwd_dq_kernel<128, false, 8, true>", "bwd_dq_prep_noncausal"),
     "bwd_dkdv": ("fa::bwd_dkdv_pair_kernel<128, false, false>", "bwd_dkdv_noncausal"),
-    "bwd_dq": ("fa::bwd_dq_kernel<128, false, 8>", "bwd_dq_noncausal"),
 }
 
 

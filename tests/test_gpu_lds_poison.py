@@ -14,8 +14,10 @@ this check removes.
 
 The shapes cover every kernel and launch form: the forward at d = 64 and 128
 with 4- and 8-wave workgroups, ragged and causal tails, the fp32 forward, the
-backward (prep, the 4-wave d = 64 dK/dV kernel, the paired d = 128 kernel
-whose dS wave lags its P wave by one tile, the dQ kernel), the split grouped-
+backward (the dQ kernel with the row statistics formed in it, the 4-wave
+d = 64 dK/dV kernel, the paired d = 128 kernel whose dS wave lags its P wave
+by one tile; the separate preprocess through the stage tests of the suite
+run against this build), the split grouped-
 query dK/dV with its reduction, decoding and the FP8 forward.
 """
 

@@ -37,8 +37,7 @@ def _fake_profile(root):
                + [(i, copy, 131072.0) for i in (2, 3, 4)])
     _write_run(root, "copy", "WRITE_SIZE", [(1, "__amd_rocclr_fillBufferAligned", 262144.0)]
                + [(i, copy, 262144.0) for i in (2, 3, 4)])
-    values = {"fwd": (1000.0, 300.0), "bwd_prep": (200.0, 50.0), "bwd_dkdv": (3000.0, 600.0),
-              "bwd_dq": (2000.0, 400.0)}
+    values = {"fwd": (1000.0, 300.0), "bwd_dq_prep": (2000.0, 400.0), "bwd_dkdv": (3000.0, 600.0)}
     for stage, (kernel, _) in traffic.STAGES.items():
         f, w = values[stage]
         for counter, v in (("FETCH_SIZE", f), ("WRITE_SIZE", w)):
@@ -80,7 +79,7 @@ def test_traffic_missing_run_is_an_error(tmp_path):
 
 
 def test_source_hash_separates_forward_and_backward():
-    hf, hb = traffic.kernel_source_hash("fwd_noncausal"), traffic.kernel_source_hash("bwd_dq_noncausal")
+    hf, hb = traffic.kernel_source_hash("fwd_noncausal"), traffic.kernel_source_hash("bwd_dq_prep_noncausal")
     assert len(hf) == 64 and len(hb) == 64 and hf != hb
     assert traffic.kernel_source_hash("bwd_dkdv_noncausal") == hb
 
