@@ -115,9 +115,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int S = GQA ? a.gsplit : 1;
     const int GS = G / S;
     const int nk = (N + BK - 1) / BK;
-    const int r = xcd_remap(blockIdx.x, nk * B * Hkv * S);
-    const int unit = r / nk;
-    const int kb = r - unit * nk;        // causal: low key blocks see the most query tiles, so go first
+    int unit, kb;                        // causal: low key blocks see the most query tiles, so go first
+    work_item(blockIdx.x, nk, B * Hkv * S, CAUSAL, unit, kb);
     const int bhk = GQA ? unit / S : unit;
     const int sp = GQA ? unit - bhk * S : 0;   // part of the head group
     const int b = bhk / Hkv, hk = bhk - b * Hkv;
@@ -461,9 +460,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     const int S = GQA ? a.gsplit : 1;
     const int GS = G / S;
     const int nk = (N + BK - 1) / BK;
-    const int r = xcd_remap(blockIdx.x, nk * B * Hkv * S);
-    const int unit = r / nk;
-    const int kb = r - unit * nk;        // causal: low key blocks see the most query tiles, so go first
+    int unit, kb;                        // causal: low key blocks see the most query tiles, so go first
+    work_item(blockIdx.x, nk, B * Hkv * S, CAUSAL, unit, kb);
     const int bhk = GQA ? unit / S : unit;
     const int sp = GQA ? unit - bhk * S : 0;   // part of the head group
     const int b = bhk / Hkv, hk = bhk - b * Hkv;
@@ -838,9 +836,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void bwd_dq_kernel(B
     const int B = a.B, H = a.H, N = a.N;
     const int npad = (N + 63) & ~63;
     const int nq = (N + BM - 1) / BM;
-    const int r = xcd_remap(blockIdx.x, nq * B * H);
-    const int bh = r / nq;
-    int qb = r - bh * nq;
+    int bh, qb;
+    work_item(blockIdx.x, nq, B * H, CAUSAL, bh, qb);
     if (CAUSAL) qb = nq - 1 - qb;        // longest rows first
     const int b = bh / H, h = bh - b * H;
 

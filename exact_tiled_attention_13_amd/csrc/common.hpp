@@ -130,6 +130,32 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
     return x * per + (x < rem ? x : rem) + k;
 }
 
+// Work item of workgroup `id` in a grid of `units` x `nb` items: a unit is a
+// head (or a K/V head and part of its query-head group), and its nb blocks
+// are its query or key blocks. XCD x gets a contiguous range of items
+// (xcd_remap), so the units of that range run on one XCD and share its L2.
+// blk is the block's rank in the order the XCD should start them. Without the
+// causal mask every block costs the same and a unit's blocks run together
+// (unit-major). Under the mask (ranked), rank 0 is the heaviest block; when
+// the units split evenly over the 8 XCDs, each XCD starts its units'
+// blocks rank-major -- the heaviest block of every unit first -- so that its
+// CUs get the work longest-first. Unit by unit instead, with several units per
+// XCD, the heavy blocks of an XCD's last unit start only after the light ones
+// of the others and finish alone, leaving the other CUs idle.
+__device__ __forceinline__ void work_item(int id, int nb, int units, bool ranked, int& unit, int& blk) {
+    const int r = xcd_remap(id, nb * units);
+    if (ranked && (units & 7) == 0) {
+        const int ux = units >> 3;       // units per XCD
+        const int per = ux * nb;
+        const int x = r / per, j = r - x * per;
+        blk = j / ux;
+        unit = x * ux + (j - blk * ux);
+    } else {
+        unit = r / nb;
+        blk = r - unit * nb;
+    }
+}
+
 // Combine a per-lane value with the one held by lane (lane ^ 32): in the
 // 32x32 accumulator layout the two halves of a wave64 hold the same column.
 // v_permlane32_swap exchanges the upper 32 lanes of one operand with the

@@ -116,9 +116,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
 
     const int B = a.B, H = a.H, N = a.N;
     const int nq = (N + BM - 1) / BM;
-    const int r = xcd_remap(blockIdx.x, nq * B * H);
-    const int bh = r / nq;
-    int qb = r - bh * nq;
+    int bh, qb;
+    work_item(blockIdx.x, nq, B * H, CAUSAL, bh, qb);
     if (CAUSAL) qb = nq - 1 - qb;         // longest rows first
     const int b = bh / H, h = bh - b * H;
 
