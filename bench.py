@@ -429,6 +429,11 @@ def main():
 
     out["mfma_microbench"] = {f"operands_{name}": micro.mfma_bf16(dev, mode=m)
                               for name, m in (("constant", 0), ("random", 1))}
+    # Each pass's rate as a share of that measured changing-operand rate: how much of what this box's
+    # matrix cores sustain under the power limit the pass gets (context for box-to-box differences).
+    mf = out["mfma_microbench"]["operands_random"]["tflops"]
+    for p_ in passes.values():
+        p_["frac_measured_mfma"] = round(p_["tflops"] / mf, 4) if mf > 0 else None
     # Report-only: the other 16k-token workloads (head dim 64 at 16k tokens,
     # grouped-query attention at 16k tokens, the short-sequence and mid-length
     # configurations, the batched backward), decoding against a 16k-token
