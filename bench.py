@@ -279,7 +279,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the kernels shard by heads with no communication, see DESIGN.md)", file=sys.stderr)
+              "(across GPUs the kernels would shard by heads, with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import torch
