@@ -20,9 +20,9 @@
 //                 accumulator each lane holds one query column (lane % 32) and
 //                 16 keys, so the row max / row sum are in-lane plus one
 //                 exchange with lane ^ 32.
-//   In the 8-wave form (d = 128 beyond 1024 tokens) waves 4-7 run half a step
-//   behind waves 0-3 (ping-pong), and a tile's row maximum is only taken when
-//   its probabilities outgrow the running one (kSumLimit below).
+//   In the 8-wave form (long sequences, see kFwdShortN) waves 4-7 run half
+//   a step behind waves 0-3 (ping-pong), and a tile's row maximum is only
+//   taken when its probabilities outgrow the running one (kSumLimit below).
 //   O^T += V^T P^T  A = V^T tile from LDS (stored transposed, keys permuted
 //                 within 16-key chunks to the order the accumulator holds
 //                 them in), B = P^T converted in registers from the S^T
@@ -59,18 +59,24 @@ constexpr float kTau = 8.0f;
 constexpr float kSumLimit = 65536.0f;
 
 // d = 128 sequences up to this length use 4-wave workgroups (see
-// fwd_bf16_kernel); d = 64 always does (measured on MI355X: 1-25% faster at
-// every length for d = 64). For d = 128 the 8-wave ping-pong form wins
-// beyond 1024 tokens (4-7% at 1500-2048 tokens without the mask, 7% at 1536
-// with it, 4-8% at 2730-4096); at 512-1024 tokens the two are level within
-// 2%.
+// fwd_bf16_kernel), longer ones the 8-wave ping-pong form, which wins
+// beyond 1024 tokens (measured on MI355X: 4-7% at 1500-2048 tokens without
+// the mask, 7% at 1536 with it, 4-8% at 2730-4096; at 512-1024 tokens the
+// two are level within 2%).
 constexpr int kFwdShortN = 1024;
+// d = 64 uses the 8-wave form from this length on, when its grid gives every
+// CU at least two workgroups (kFwdMinWgs8): 5-6% faster without the mask and
+// 2-10% with it at 4096-16384 tokens. Below, or on smaller grids, the 4-wave
+// form with three workgroups per CU is faster (13% at 3000 tokens on 384
+// 8-wave workgroups; level at 2048).
+constexpr int kFwdShortN64 = 4096;
+constexpr long long kFwdMinWgs8 = 512;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void fwd_bf16_kernel(FwdArgs a) {
     // NW waves per workgroup: 8 (two per SIMD, one workgroup per CU), or 4
     // with two workgroups sharing a CU (three at d = 64, within 168 VGPRs
     // and 48 KB of LDS each), so that one's start-up and tail overlap the
@@ -82,13 +88,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     constexpr int RB = D * 2;             // bytes per K/V row
     constexpr int TILE = BN * RB;         // bytes per K or V tile
     constexpr int NINST = TILE / 1024;    // 1 KB direct-to-LDS wave loads per tile
-    // Ping-pong (8 waves at d = 128, the workgroup alone on its CU): waves
+    // Ping-pong (8 waves, the workgroup alone on its CU): waves
     // 4-7 run half a step behind waves 0-3 (see the main loop), so that on
     // each SIMD, which holds one wave of each half, one wave's exponentials
     // overlap the other's P V products instead of both waves reaching the
     // same phase together after every barrier. Waves 0-3 issue all the tile
     // loads.
-    constexpr bool PP = D == 128 && NW == 8;
+    constexpr bool PP = NW == 8;
     constexpr int NL = PP ? NW / 2 : NW;  // waves that issue the tile loads
     constexpr int IPW = NINST / NL;       // ... per loading wave
     constexpr int RPI = 1024 / RB;        // rows covered by one such load
@@ -107,8 +113,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
     // XOR-swizzled per row (see swk / swv) so that the MFMA operand reads are
     // free of bank conflicts.
     // Q enters through LDS as well (see below) where the extra LDS still
-    // leaves the workgroup's occupancy unchanged: not for d = 128 with four
-    // waves, whose two workgroups per CU already take 128 KB.
+    // leaves the workgroup's occupancy unchanged: at d = 64 (80 KB for the
+    // 8-wave form, alone on its CU), not at d = 128, whose four-wave
+    // workgroups already take 128 KB per CU and eight-wave ones 96 KB.
     constexpr bool QLDS = D == 64;
     constexpr int QST = QLDS ? NW * 32 * RB : 0;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[(2 + NVB) * TILE + QST];
@@ -671,12 +678,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 8 / NW) void fwd_bf16_kernel
 
 template <int D, bool CAUSAL>
 static hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    if constexpr (D == 128) {
-        if (a.N > kFwdShortN) {
-            const long long grid = (long long)((a.N + 255) / 256) * a.B * a.H;
-            hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8>), dim3((unsigned)grid), dim3(512), 0, stream, a);
-            return hipGetLastError();
-        }
+    const long long grid8 = (long long)((a.N + 255) / 256) * a.B * a.H;
+    const bool eight = D == 128 ? a.N > kFwdShortN : (a.N >= kFwdShortN64 && grid8 >= kFwdMinWgs8);
+    if (eight) {
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8>), dim3((unsigned)grid8), dim3(512), 0, stream, a);
+        return hipGetLastError();
     }
     const long long grid = (long long)((a.N + 127) / 128) * a.B * a.H;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a);

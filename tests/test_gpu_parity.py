@@ -89,6 +89,49 @@ def test_fwd_bf16_rising_scores(causal):
     assert aerr(f64(lse), rl) <= TOL_LSE_BF16
 
 
+def _sampled_rows_check(q, k, v, causal, scale, heads, nrows, seed):
+    o, lse = (t.cpu() for t in run_fwd(q, k, v, causal, scale))
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for i, (b, h) in enumerate(heads):
+        rows = sample_rows(q.shape[1], nrows, seed=seed + i)
+        ro, rl = attn_fwd_rows(q[b, :, h].double().numpy(), k[b, :, h].double().numpy(),
+                               v[b, :, h].double().numpy(), rows, causal, scale)
+        got_o.append(f64(o[b, rows, h]))
+        ref_o.append(ro)
+        got_l.append(f64(lse[b, h, rows]))
+        ref_l.append(rl)
+    assert nerr(np.concatenate(got_o), np.concatenate(ref_o)) <= TOL_O_BF16
+    assert aerr(np.concatenate(got_l), np.concatenate(ref_l)) <= TOL_LSE_BF16
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_bf16_long_d64_eight_wave(causal):
+    """Head dim 64 from 4096 tokens on, on a grid of at least 512 eight-wave workgroups, runs the
+    8-wave ping-pong forward (shorter sequences and smaller grids the 4-wave one): 2 x 16 heads x
+    4097 tokens (17 query blocks of 256 per head, the last one row long) on sampled rows of three
+    heads, the last row included."""
+    N, d = 4097, 64
+    q, k, v = make_qkv(2, 16, N, d, "bf16", seed=4097 + causal)
+    s = float(np.float32(d ** -0.5))
+    print(f"d64 eight-wave forward causal={causal}", flush=True)
+    _sampled_rows_check(q, k, v, causal, s, heads=[(0, 0), (1, 7), (1, 15)], nrows=256, seed=77)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_bf16_rising_scores_d64(causal):
+    """The rescale path of the 8-wave forward at d = 64 (1 x 32 heads x 4096 tokens, 512 eight-wave
+    workgroups): scores rise by about 16 (base 2) from each 64-key tile to the next, so every tile
+    outgrows the running maximum; sampled rows of three heads."""
+    N, d, H = 4096, 64, 32
+    g = torch.Generator().manual_seed(6101 + causal)
+    q = (0.1 + 0.02 * torch.randn(1, N, H, d, generator=g)).to(torch.bfloat16)
+    ramp = (14.0 * (torch.arange(N) // 64)).view(1, N, 1, 1)
+    k = (ramp + torch.randn(1, N, H, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(1, N, H, d, generator=g).to(torch.bfloat16)
+    s = float(np.float32(d ** -0.5))
+    _sampled_rows_check(q, k, v, causal, s, heads=[(0, 0), (0, 13), (0, 31)], nrows=192, seed=91)
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_bf16_other_scales(scale, causal):
