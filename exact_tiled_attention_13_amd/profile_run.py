@@ -3,8 +3,9 @@
 Usage: python -m exact_tiled_attention_13_amd.profile_run WHAT [--causal] [--reps R]
 WHAT is one of fwd, bwd_prep, bwd_dq, bwd_dq_prep (dQ with the preprocess
 fused, as attn_bwd runs it), bwd_dkdv, step (fwd, bwd_dq_prep, bwd_dkdv: one
-forward and backward as bench.py times them), fp8, decode,
-or copy (a plain device-to-device copy of 256 MiB through torch, used to
+forward and backward as bench.py times them), fp8, decode, fwd_short (the
+forward of the short-sequence workload: batch 32, 32 heads, 512 tokens, head
+dim 64), or copy (a plain device-to-device copy of 256 MiB through torch, used to
 calibrate the HBM byte counters: it reads and writes exactly 256 MiB per
 launch).
 Workloads: batch 1, 16 heads, 16384 tokens, head dim 128, seeded inputs, bf16
@@ -24,7 +25,7 @@ if ROOT not in sys.path:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("what", choices=["fwd", "bwd_prep", "bwd_dq", "bwd_dq_prep", "bwd_dkdv", "step", "fp8",
-                                        "decode", "copy"])
+                                        "decode", "fwd_short", "copy"])
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--reps", type=int, default=3)
     args = ap.parse_args()
@@ -68,6 +69,18 @@ def main():
             fa.attn_decode(q, k, v, args.causal, w.scale, o=o, lse=lse, ws=ws)
         torch.cuda.synchronize()
         print(f"decode causal={args.causal} done", flush=True)
+        return
+
+    if args.what == "fwd_short":
+        from exact_tiled_attention_13_amd.inputs import WORKLOADS
+
+        w = WORKLOADS["fwd_bf16_b32_h32_n512_d64"]
+        q, k, v = (x.to(dev) for x in make_workload(w))
+        o, lse = fa.attn_fwd(q, k, v, args.causal, w.scale)
+        for _ in range(args.reps):
+            fa.attn_fwd(q, k, v, args.causal, w.scale, o=o, lse=lse)
+        torch.cuda.synchronize()
+        print(f"fwd_short causal={args.causal} done", flush=True)
         return
 
     w = BWD_LONG
