@@ -324,6 +324,33 @@ def test_gqa_bf16_ragged_long_d128(causal):
     assert nerr(f64(dv), rv) <= TOL_GRAD_BF16
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_bf16_long_d64_eight_wave_forward(causal):
+    """The 8-wave d = 64 forward with grouped-query heads: 32 query heads on 4 K/V heads, 4096 tokens
+    (512 eight-wave workgroups); sampled rows of query heads in three groups against the oracle on
+    their K/V head."""
+    from exact_tiled_attention_13_amd.inputs import make_gqa
+    B, H, Hkv, N, d = 1, 32, 4, 4096, 64
+    q, k, v = make_gqa(B, H, Hkv, N, d, "bf16", seed=4096 + causal)
+    s = float(np.float32(d ** -0.5))
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o, lse = fa.attn_fwd_gqa(qd, kd, vd, causal, s)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    G = H // Hkv
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for i, h in enumerate([0, 13, 31]):
+        rows = sample_rows(N, 192, seed=300 + i)
+        ro, rl = attn_fwd_rows(q[0, :, h].double().numpy(), k[0, :, h // G].double().numpy(),
+                               v[0, :, h // G].double().numpy(), rows, causal, s)
+        got_o.append(f64(o[0, rows, h]))
+        ref_o.append(ro)
+        got_l.append(f64(lse[0, h, rows]))
+        ref_l.append(rl)
+    assert nerr(np.concatenate(got_o), np.concatenate(ref_o)) <= TOL_O_BF16
+    assert aerr(np.concatenate(got_l), np.concatenate(ref_l)) <= TOL_LSE_BF16
+
+
 def test_gqa_with_hkv_equal_h_is_bitwise_mha():
     q, k, v, do = make_qkv(1, 3, 300, 64, "bf16", seed=77, with_do=True)
     s = float(np.float32(0.125))
