@@ -210,6 +210,41 @@ def time_passes(w, reps=10, warmup=3):
     return out
 
 
+def time_sweep(reps=10, warmup=3):
+    """Report-only: the pages' kernel benchmark grid (inputs.SWEEP_*): for each sequence length, head dim
+    and mask, the forward and the backward at 16k tokens per batch, timed as time_passes times them."""
+    import torch
+
+    import exact_tiled_attention_13_amd as fa
+    from exact_tiled_attention_13_amd.inputs import SWEEP_D, SWEEP_N, make_qkv_device, sweep_shape
+
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev).cuda_stream
+    p = lambda t: t.data_ptr()
+    out = {}
+    for d in SWEEP_D:
+        for N in SWEEP_N:
+            B, H, _, _ = sweep_shape(N, d)
+            q, k, v, do = make_qkv_device(B, H, N, d, seed=2000 + N + d, device=dev)
+            scale = float(torch.tensor(d ** -0.5, dtype=torch.float32).item())
+            ws = fa.workspace(B, H, N, d, dev)
+            for c in (False, True):
+                o, lse = fa.attn_fwd(q, k, v, c, scale)
+                dq, dk, dv = fa.attn_bwd(q, k, v, o, do, lse, c, scale, workspace=ws)
+                fwd = _raw("attn_fwd", p(q), p(k), p(v), p(o), p(lse), B, H, N, d, int(c), scale, st)
+                bwd = _raw("attn_bwd", p(q), p(k), p(v), p(o), p(do), p(lse), p(dq), p(dk), p(dv), p(ws),
+                           ws.numel(), B, H, N, d, int(c), scale, st)
+                entry = {"B": B, "H": H}
+                for name, f, mult in (("fwd", fwd, 1.0), ("bwd", bwd, 2.5)):
+                    ms = _time_calls(f, reps, warmup)
+                    flop = mult * counted_fwd(B, H, N, d, c)
+                    entry[f"{name}_ms"] = round(ms, 4)
+                    entry[f"{name}_frac_bf16_peak"] = round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+                out[f"n{N}_d{d}_{'causal' if c else 'noncausal'}"] = entry
+            del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
+
+
 def decode_bytes(B, H, Hkv, Nq, Nk, d):
     """Compulsory HBM bytes of one bf16 decode call: K and V of the cache, Q, O (bf16) and LSE (fp32)."""
     return 2.0 * 2 * B * Nk * Hkv * d + 2.0 * 2 * B * Nq * H * d + 4.0 * B * H * Nq
@@ -452,6 +487,8 @@ def main():
 
         report[FP8_LONG.name] = time_fp8(FP8_LONG)
         out["other_workloads"] = report
+        # The pages' sweep: sequence lengths 512 .. 16384 at 16k tokens per batch, d = 64 and 128, both masks.
+        out["sweep_16k_tokens"] = time_sweep()
     refs = {}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale, refs=refs)

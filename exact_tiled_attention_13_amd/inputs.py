@@ -75,6 +75,32 @@ LONG_D64 = Workload("bwd_bf16_b1_h32_n16384_d64", "bf16", 1, 32, 16384, 64, (Fal
 LONG_GQA = Workload("bwd_bf16_b1_h16_hkv2_n16384_d128", "bf16", 1, 16, 16384, 128, (False, True), True, 1007, Hkv=2)
 
 
+# The kernel benchmark grid of that section: 16k tokens per batch with
+# H * d = 2048, sequence lengths 512 .. 16384 (B = 16384 / N), head dims 64
+# (32 heads) and 128 (16 heads), both masks. Timed in the benchmark's report,
+# forward and backward, on inputs drawn on the device (timing only: the
+# outputs are not compared there; parity at these shapes is the tests').
+SWEEP_N = (512, 1024, 2048, 4096, 8192, 16384)
+SWEEP_D = (64, 128)
+SWEEP_TOKENS = 16384
+SWEEP_HIDDEN = 2048
+
+
+def sweep_shape(N: int, d: int):
+    """(B, H, N, d) of the sweep point with sequence length N and head dim d."""
+    return SWEEP_TOKENS // N, SWEEP_HIDDEN // d, N, d
+
+
+def make_qkv_device(B: int, H: int, N: int, d: int, seed: int, device, with_do: bool = True):
+    """Q, K, V (and dO) [B, N, H, d] drawn on `device` by a generator seeded there: randn float32 rounded to
+    bfloat16, in that order. For timing runs whose outputs nothing compares (drawing the largest shapes on
+    the CPU takes seconds)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    n = 4 if with_do else 3
+    return tuple(torch.randn(B, N, H, d, dtype=torch.float32, generator=g, device=device).to(torch.bfloat16)
+                 for _ in range(n))
+
+
 @dataclass(frozen=True)
 class DecodeWorkload:
     """Decoding: Nq new query rows per sequence against a cache of Nk keys and values."""
