@@ -310,7 +310,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-report", action="store_true", help="skip the report-only timings of the other workloads")
+    ap.add_argument("--no-report", action="store_true", help="skip the report-only timings (the other workloads and the sweep)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
